@@ -1,0 +1,6 @@
+"""fp64 CPU oracle for the attention-JVP hot path (test infrastructure only).
+
+Only the tests, the graft smoke check and the benchmark's cpu_baseline leg may
+import this package.  The product library never does.
+"""
+from .attn_jvp import attention_jvp, attention_jvp_head  # noqa: F401
