@@ -1,0 +1,123 @@
+// Device-side helpers shared by the bf16 and fp32 attention-JVP kernels (gfx950).
+//
+// Conventions used throughout:
+//  * A wave (64 lanes) owns 32 query rows.  Lane l serves query n = l % 32 and
+//    "half" hh = l / 32.  All products are computed transposed (keys or head
+//    dimension in the MFMA M slot, queries in the N slot), so the 32x32 MFMA
+//    accumulator layout puts one query per lane:
+//        accumulator register r of lane l  ->  row 8*(r/4) + 4*hh + r%4, column n.
+//    Per-query statistics are therefore per-lane values; the two halves of a
+//    query (lanes l and l^32) hold disjoint key subsets and are combined with
+//    v_permlane32_swap.
+//  * Online softmax runs in the log2 domain: x = S * scale * log2(e).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnjvp {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaveRows = 32;              // query rows per wave
+constexpr int kWaves = 4;                  // waves per workgroup
+constexpr int kThreads = kWaves * 64;      // 256
+constexpr int kBlockRows = kWaves * kWaveRows;  // 128 query rows per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Rescale threshold (log2 units): the running max used for exponentiation is
+// only moved when a row's max grows by more than this, so exp2 arguments stay
+// <= kRescaleSlack and p <= 2^8.  Softmax is shift invariant, so the result is
+// the same up to rounding.
+constexpr float kRescaleSlack = 8.0f;
+
+// Buffer resource over [base, base + bytes): loads past the end return 0 and
+// stores past the end are dropped by the hardware range check.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ inline void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+__device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ inline void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
+// Renumber them so that XCD x owns one contiguous range of logical ids: the
+// query tiles of one head then run on the same XCD and share K/V in its L2.
+__device__ inline int xcd_logical_block(int hw_id, int n_blocks) {
+  const int per = n_blocks / 8, rem = n_blocks % 8;
+  const int x = hw_id % 8, slot = hw_id / 8;
+  return (x < rem) ? x * (per + 1) + slot : rem * (per + 1) + (x - rem) * per + slot;
+}
+
+// Reductions across the two 32-lane halves (lane l with lane l ^ 32).
+__device__ inline float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Key offset (within a 32-key block) held by accumulator register r of half hh.
+__device__ inline int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
+
+// Running per-query state.  m: max (log2 domain) used for exponentiation;
+// l, a: this lane's partial sums of p and p*tS over its half of the keys.
+struct RowState {
+  float m;
+  float l;
+  float a;
+};
+
+// Mask keys >= valid (tile-relative) of a tile made of NB 32-key blocks.
+template <int NB>
+__device__ inline void mask_tail(f32x16 (&s)[NB], int valid, int hh) {
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * b + acc_row(r, hh) >= valid) s[b][r] = -INFINITY;
+}
+
+// Tile max of the raw logits, combined over both halves, in the log2 domain.
+template <int NB>
+__device__ inline float tile_max_log2(const f32x16 (&s)[NB], float c) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[b][r]);
+  return xhalf_max(mx) * c;
+}
+
+// Decide whether this tile moves the exponent base.  Returns true (wave-uniform)
+// when at least one row must rescale; alpha is then that row's factor (1 for the
+// others) and st.m has been updated.  st.l and st.a are rescaled here; the
+// caller rescales its matrix accumulators by alpha.
+__device__ inline bool update_max(RowState& st, float mt, float& alpha) {
+  const bool need = mt > st.m + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(need) == 0) return false;
+  const float m_new = need ? mt : st.m;
+  alpha = need ? fast_exp2(st.m - m_new) : 1.0f;
+  st.m = m_new;
+  st.l *= alpha;
+  st.a *= alpha;
+  return true;
+}
+
+}  // namespace attnjvp

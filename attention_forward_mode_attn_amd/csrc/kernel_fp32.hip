@@ -1,0 +1,237 @@
+// fp32 attention forward + JVP on gfx950 matrix cores (v_mfma_f32_32x32x2_f32).
+//
+// Same tiling, transposed products and online softmax as the bf16 kernel, in
+// IEEE fp32 throughout (fp32 MFMA has no reduced-precision inputs).  Each MFMA
+// contracts two elements, one per half-wave, so:
+//  * S^T = K Q^T pairs head dims c and c + d/2 (half hh supplies dim
+//    hh*d/2 + c): each lane keeps d/2 of its query's Q and tQ values;
+//  * O^T += V^T P^T pairs the two keys that accumulator register r holds in the
+//    two halves, so P comes straight from the S accumulator as an fp32 operand
+//    and V is read row-major from LDS (32 consecutive dims per half-wave).
+// Tiles hold 32 keys (one accumulator block) to bound register use.
+#include "device_common.h"
+#include "launch.h"
+
+namespace attnjvp {
+namespace {
+
+constexpr int kBcF = 32;  // keys per tile
+
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* tq;
+  const void* tk;
+  const void* tv;
+  void* o;
+  void* to;
+  float* lse;
+  int Lq, Lk, n_qtiles, n_blocks;
+  float scale;
+};
+
+template <int D>
+struct Cfg {
+  static constexpr int kTile = kBcF * D * 4;           // bytes of one tile, [key][dim]
+  static constexpr int kStage = 4 * kTile;             // K, tK, V, tV
+  static constexpr int kUnits = kBcF * D / 4;          // 16-byte units in a tile
+  static constexpr int kPerThread = kUnits / kThreads;
+  static constexpr int kBlocksD = D / 32;
+  static_assert(kUnits % kThreads == 0, "tile split");
+};
+
+// K/tK rows are XOR-swizzled by 16-byte unit so that 32 lanes reading the same
+// column of 32 different rows hit distinct banks.  V/tV rows are not swizzled:
+// their readers take 32 consecutive floats of one row.
+template <int D>
+__device__ inline uint32_t k_off(int r, int u) {
+  return r * (D * 4) + ((u ^ (r & 7)) << 4);
+}
+
+__device__ inline f32x16 mfma(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+struct Staging {
+  u32x4 x[4][Cfg<D>::kPerThread];
+};
+
+template <int D>
+__device__ inline void issue_tile_loads(Staging<D>& sg, const __amdgpu_buffer_rsrc_t (&r)[4], int key0, int t) {
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+    for (int i = 0; i < Cfg<D>::kPerThread; ++i) {
+      const int e = t + kThreads * i;
+      sg.x[tn][i] = buf_load16(r[tn], ((uint32_t)key0 * D + e * 4) * 4);
+    }
+}
+
+template <int D>
+__device__ inline void store_tile(const Staging<D>& sg, char* stage, int t) {
+#pragma unroll
+  for (int i = 0; i < Cfg<D>::kPerThread; ++i) {
+    const int e = t + kThreads * i;
+    const int row = e / (D / 4), u = e % (D / 4);
+    *reinterpret_cast<u32x4*>(stage + k_off<D>(row, u)) = sg.x[0][i];
+    *reinterpret_cast<u32x4*>(stage + Cfg<D>::kTile + k_off<D>(row, u)) = sg.x[1][i];
+    *reinterpret_cast<u32x4*>(stage + 2 * Cfg<D>::kTile + e * 16) = sg.x[2][i];
+    *reinterpret_cast<u32x4*>(stage + 3 * Cfg<D>::kTile + e * 16) = sg.x[3][i];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_jvp_fp32_kernel(Params p) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::kStage];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6, n = lane & 31, hh = lane >> 5;
+  const int blk = xcd_logical_block(blockIdx.x, p.n_blocks);
+  const int bh = blk / p.n_qtiles, qt = blk % p.n_qtiles;
+  const int Lq = p.Lq, Lk = p.Lk;
+
+  const size_t qhead = (size_t)bh * Lq * D * 4, khead = (size_t)bh * Lk * D * 4;
+  const uint32_t qbytes = (uint32_t)Lq * D * 4, kbytes = (uint32_t)Lk * D * 4;
+  const auto rq = make_rsrc((const char*)p.q + qhead, qbytes);
+  const auto rtq = make_rsrc((const char*)p.tq + qhead, qbytes);
+  const __amdgpu_buffer_rsrc_t rkv[4] = {
+      make_rsrc((const char*)p.k + khead, kbytes), make_rsrc((const char*)p.tk + khead, kbytes),
+      make_rsrc((const char*)p.v + khead, kbytes), make_rsrc((const char*)p.tv + khead, kbytes)};
+
+  // Lane (n, hh) keeps dims hh*D/2 .. hh*D/2 + D/2 - 1 of its query's Q and tQ.
+  const int qrow = qt * kBlockRows + wv * kWaveRows + n;
+  float qf[D / 2], tqf[D / 2];
+#pragma unroll
+  for (int i = 0; i < D / 8; ++i) {
+    const uint32_t off = ((uint32_t)qrow * D + hh * (D / 2) + 4 * i) * 4;
+    const u32x4 a = buf_load16(rq, off), b = buf_load16(rtq, off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qf[4 * i + e] = __uint_as_float(a[e]);
+      tqf[4 * i + e] = __uint_as_float(b[e]);
+    }
+  }
+
+  f32x16 acc_o[C::kBlocksD], acc_t[C::kBlocksD];
+#pragma unroll
+  for (int b = 0; b < C::kBlocksD; ++b) {
+    acc_o[b] = f32x16{};
+    acc_t[b] = f32x16{};
+  }
+  RowState st = {-INFINITY, 0.0f, 0.0f};
+  const float scale = p.scale;
+  const float c2 = scale * kLog2e;
+  const int sw = n & 7;
+
+  const int nt = (Lk + kBcF - 1) / kBcF;
+  Staging<D> sg;
+  issue_tile_loads<D>(sg, rkv, 0, t);
+  store_tile<D>(sg, smem, t);
+  __syncthreads();
+
+  for (int j = 0; j < nt; ++j) {
+    const char* cur = smem + (j & 1) * C::kStage;
+    if (j + 1 < nt) issue_tile_loads<D>(sg, rkv, (j + 1) * kBcF, t);
+
+    f32x16 s[1] = {f32x16{}}, ts[1] = {f32x16{}};
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) {
+      // unit hh*D/8 + i of row n holds dims hh*D/2 + 4i .. +3
+      const uint32_t off = n * (D * 4) + (((hh * (D / 8) + i) ^ sw) << 4);
+      const f32x4 kk = *reinterpret_cast<const f32x4*>(cur + off);
+      const f32x4 tkk = *reinterpret_cast<const f32x4*>(cur + C::kTile + off);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[0] = mfma(kk[e], qf[4 * i + e], s[0]);
+        ts[0] = mfma(kk[e], tqf[4 * i + e], ts[0]);
+        ts[0] = mfma(tkk[e], qf[4 * i + e], ts[0]);
+      }
+    }
+
+    if (j == nt - 1 && (Lk % kBcF) != 0) mask_tail<1>(s, Lk - j * kBcF, hh);
+    float alpha;
+    if (update_max(st, tile_max_log2<1>(s, c2), alpha)) {
+#pragma unroll
+      for (int b = 0; b < C::kBlocksD; ++b) {
+        acc_o[b] *= alpha;
+        acc_t[b] *= alpha;
+      }
+    }
+    float pv[16], ptv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pv[r] = fast_exp2(__builtin_fmaf(s[0][r], c2, -st.m));
+      ptv[r] = pv[r] * (ts[0][r] * scale);
+      st.l += pv[r];
+      st.a += ptv[r];
+    }
+
+    const char* vbase = cur + 2 * C::kTile;
+    const char* tvbase = cur + 3 * C::kTile;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = acc_row(r, hh);
+#pragma unroll
+      for (int b = 0; b < C::kBlocksD; ++b) {
+        const uint32_t off = (key * D + 32 * b + n) * 4;
+        const float vv = *reinterpret_cast<const float*>(vbase + off);
+        const float tvv = *reinterpret_cast<const float*>(tvbase + off);
+        acc_o[b] = mfma(vv, pv[r], acc_o[b]);
+        acc_t[b] = mfma(tvv, pv[r], acc_t[b]);
+        acc_t[b] = mfma(vv, ptv[r], acc_t[b]);
+      }
+    }
+
+    if (j + 1 < nt) store_tile<D>(sg, smem + ((j + 1) & 1) * C::kStage, t);
+    __syncthreads();
+  }
+
+  const float l = xhalf_sum(st.l), a = xhalf_sum(st.a);
+  const float inv = 1.0f / l, mu = a * inv;
+  const auto ro = make_rsrc((const char*)p.o + qhead, qbytes);
+  const auto rto = make_rsrc((const char*)p.to + qhead, qbytes);
+#pragma unroll
+  for (int b = 0; b < C::kBlocksD; ++b) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x4 ov, tv4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = acc_o[b][4 * g + i];
+        ov[i] = __float_as_uint(x * inv);
+        tv4[i] = __float_as_uint((acc_t[b][4 * g + i] - mu * x) * inv);
+      }
+      const uint32_t off = ((uint32_t)qrow * D + 32 * b + 8 * g + 4 * hh) * 4;
+      buf_store16(ro, off, ov);
+      buf_store16(rto, off, tv4);
+    }
+  }
+  if (hh == 0) {
+    const auto rl = make_rsrc((const char*)p.lse + (size_t)bh * Lq * 4, (uint32_t)Lq * 4);
+    buf_store4(rl, (uint32_t)qrow * 4, (st.m + __builtin_amdgcn_logf(l)) * kLn2);
+  }
+}
+
+template <int D>
+hipError_t launch(const Problem& pr, hipStream_t stream) {
+  Params p;
+  p.q = pr.q; p.k = pr.k; p.v = pr.v; p.tq = pr.tq; p.tk = pr.tk; p.tv = pr.tv;
+  p.o = pr.o; p.to = pr.to; p.lse = pr.lse;
+  p.Lq = pr.Lq; p.Lk = pr.Lk; p.scale = pr.scale;
+  p.n_qtiles = (pr.Lq + kBlockRows - 1) / kBlockRows;
+  p.n_blocks = pr.B * pr.H * p.n_qtiles;
+  hipLaunchKernelGGL(attn_jvp_fp32_kernel<D>, dim3(p.n_blocks), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fp32(const Problem& p, hipStream_t stream) {
+  return p.d == 128 ? launch<128>(p, stream) : launch<64>(p, stream);
+}
+
+}  // namespace attnjvp

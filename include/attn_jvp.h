@@ -1,0 +1,108 @@
+/*
+ * attn_jvp.h — C ABI of the MI355X (gfx950) attention forward + JVP library.
+ *
+ * One call computes, for every (batch b, head h), softmax attention and its
+ * forward-mode derivative (Jacobian-vector product) along the tangents
+ * (tQ, tK, tV):
+ *
+ *   S   = scale * Q K^T                    P  = row-softmax(S)
+ *   O   = P V                              lse = log(sum_j exp(S_ij))  (natural log)
+ *   tS  = scale * (tQ K^T + Q tK^T)        mu = sum_j P_ij tS_ij
+ *   tO  = P tV + (P * (tS - mu)) V
+ *
+ * This is the fused "FlashAttention-2 forward with the JVP embedded" that the
+ * rCM pages describe: papernotes.org reading notes on "Large Scale Diffusion
+ * Distillation via Score-Regularized Continuous-Time Consistency", section
+ * "Key designs", item 1 (a kernel returning the attention output together with
+ * its JVP, for self- and cross-attention); ai.info summary of the same paper,
+ * "Key Contributions" item 1 and "Methodology in Plain English" (tangents
+ * carried through the same block-wise tiling, layers exposing forward/tangent
+ * functions).  The JVP itself is the Jacobian applied to the tangent (notes on
+ * "Consistent Distribution Matching for Data-Free Diffusion Distillation",
+ * prerequisites, "JVP").  Self-attention is Lq == Lk with shared sequence
+ * length; cross-attention is any Lq != Lk.
+ *
+ * Readings where the pages are silent: scale carries no tangent; lse uses the
+ * natural log of the scaled logits; there is no mask, dropout or bias.
+ */
+#ifndef ATTN_JVP_H
+#define ATTN_JVP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_JVP_VERSION 10000 /* 1.0.0 */
+
+/* Element type of q, k, v, tq, tk, tv, o and to (lse is always float32). */
+typedef enum {
+  ATTN_JVP_FP32 = 0, /* float32 in, float32 out, float32 arithmetic */
+  ATTN_JVP_BF16 = 1  /* bfloat16 in, bfloat16 out (round to nearest even),
+                        bf16 matrix products with float32 accumulation */
+} attn_jvp_dtype_t;
+
+typedef enum {
+  ATTN_JVP_OK = 0,
+  ATTN_JVP_EINVAL = 1,       /* NULL pointer, negative size, Lk == 0 with work to do,
+                                scale not finite or not > 0, unknown dtype */
+  ATTN_JVP_EUNSUPPORTED = 2, /* head dim not 64 or 128, or a size beyond the limits below */
+  ATTN_JVP_EALIGN = 3,       /* a tensor pointer not 16-byte aligned, or lse not 4-byte aligned */
+  ATTN_JVP_ELAUNCH = 4       /* the HIP launch failed (no device, bad stream, ...);
+                                attn_jvp_last_error() holds the HIP message */
+} attn_jvp_status_t;
+
+/*
+ * attn_jvp_fwd — enqueue one fused attention forward + JVP pass.
+ *
+ * Arguments
+ *   q, tq   [B, H, Lq, d]  queries and their tangent                (device, read only)
+ *   k, tk   [B, H, Lk, d]  keys and their tangent                   (device, read only)
+ *   v, tv   [B, H, Lk, d]  values and their tangent                 (device, read only)
+ *   o, to   [B, H, Lq, d]  outputs: attention output and its tangent (device, written)
+ *   lse     [B, H, Lq]     float32 row log-sum-exp of scale*QK^T     (device, written)
+ *   B, H, Lq, Lk, d        sizes; d in {64, 128}
+ *   scale                  logit scale (usually 1/sqrt(d)); finite and > 0
+ *   dtype                  attn_jvp_dtype_t for all tensors but lse
+ *   stream                 a hipStream_t passed as void*; NULL is the null stream
+ *
+ * Layout: every tensor is dense and contiguous, row-major in the order given,
+ * d innermost.  Pointers are device addresses (memory from hipMalloc or a
+ * framework allocator on the current device).
+ *
+ * Ownership: all buffers belong to the caller.  The library allocates nothing,
+ * keeps no state between calls and may be called from several host threads.
+ * Inputs are never written.  o, to and lse are fully overwritten; they must not
+ * overlap any input or each other (results are undefined if they do).
+ *
+ * Execution: the work is enqueued on `stream` and the call returns without
+ * synchronising.  For identical inputs and sizes the results are bitwise
+ * reproducible.
+ *
+ * Errors: all argument checks run on the host before any HIP call, and a
+ * failed check launches nothing.  B*H*Lq == 0 is a no-op returning ATTN_JVP_OK
+ * (pointers are then not inspected).  Limits: Lq*d and Lk*d below 2^29
+ * elements per head, B*H*ceil(Lq/128) below 2^31.  The library never aborts.
+ * Non-finite input values propagate into the outputs; they are not detected.
+ */
+int attn_jvp_fwd(const void* q, const void* k, const void* v,
+                 const void* tq, const void* tk, const void* tv,
+                 void* o, void* to, float* lse,
+                 int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 float scale, int dtype, void* stream);
+
+/* Static description of a status code ("unknown status" for others). */
+const char* attn_jvp_status_string(int status);
+
+/* Detail of the last failed call on the calling host thread ("" if none). */
+const char* attn_jvp_last_error(void);
+
+/* ATTN_JVP_VERSION of the built library. */
+int attn_jvp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_JVP_H */

@@ -1,0 +1,115 @@
+"""Host-side tests of the C ABI: symbols, status strings and argument checks.
+
+None of these launches a kernel: every call here fails a host check (or is a
+zero-size no-op) before any HIP call, as the header promises.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_forward_mode_attn_amd as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_jvp.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(A.library_path()):
+        pytest.fail("libattnjvp.so not built: run __graft_entry__.build()")
+    return A.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_jvp_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names == ["attn_jvp_fwd", "attn_jvp_last_error", "attn_jvp_status_string", "attn_jvp_version"]
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert A.attn_jvp_version() == 10000
+    assert A.attn_jvp_status_string(0) == "ok"
+    assert A.attn_jvp_status_string(A.ATTN_JVP_EUNSUPPORTED).startswith("unsupported")
+    assert A.attn_jvp_status_string(99) == "unknown status"
+
+
+FAKE = 0x10000  # 16-byte aligned; never dereferenced because every call below fails first
+
+
+def call(B=1, H=1, Lq=8, Lk=8, d=64, scale=0.125, dtype=0, ptrs=None, lse=None):
+    p = ptrs if ptrs is not None else [FAKE] * 8
+    return A.attn_jvp_fwd(*p[:6], p[6], p[7], FAKE if lse is None else lse, B, H, Lq, Lk, d, scale, dtype)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), A.ATTN_JVP_EINVAL),
+    (dict(dtype=-1), A.ATTN_JVP_EINVAL),
+    (dict(B=-1), A.ATTN_JVP_EINVAL),
+    (dict(Lk=-3), A.ATTN_JVP_EINVAL),
+    (dict(d=96), A.ATTN_JVP_EUNSUPPORTED),
+    (dict(d=256), A.ATTN_JVP_EUNSUPPORTED),
+    (dict(Lk=0), A.ATTN_JVP_EINVAL),
+    (dict(scale=float("nan")), A.ATTN_JVP_EINVAL),
+    (dict(scale=float("inf")), A.ATTN_JVP_EINVAL),
+    (dict(scale=0.0), A.ATTN_JVP_EINVAL),
+    (dict(scale=-0.1), A.ATTN_JVP_EINVAL),
+    (dict(ptrs=[FAKE] * 5 + [0] + [FAKE] * 2), A.ATTN_JVP_EINVAL),
+    (dict(ptrs=[FAKE] * 7 + [0]), A.ATTN_JVP_EINVAL),
+    (dict(lse=0), A.ATTN_JVP_EINVAL),
+    (dict(ptrs=[FAKE + 8] + [FAKE] * 7), A.ATTN_JVP_EALIGN),
+    (dict(ptrs=[FAKE] * 7 + [FAKE + 4]), A.ATTN_JVP_EALIGN),
+    (dict(lse=FAKE + 2), A.ATTN_JVP_EALIGN),
+    (dict(Lq=1 << 23, d=128), A.ATTN_JVP_EUNSUPPORTED),
+    (dict(Lk=1 << 23, d=64), A.ATTN_JVP_EUNSUPPORTED),
+    (dict(B=1 << 20, H=1 << 12, Lq=256), A.ATTN_JVP_EUNSUPPORTED),
+])
+def test_invalid_arguments_are_rejected_on_host(lib, kw, status):
+    assert call(**kw) == status
+    assert A.attn_jvp_last_error() != ""
+
+
+def test_zero_size_is_ok_without_pointers(lib):
+    nul = [0] * 8
+    assert call(B=0, ptrs=nul, lse=0) == A.ATTN_JVP_OK
+    assert call(H=0, ptrs=nul, lse=0) == A.ATTN_JVP_OK
+    assert call(Lq=0, Lk=0, ptrs=nul, lse=0) == A.ATTN_JVP_OK
+    assert A.attn_jvp_last_error() == ""
+
+
+def test_dimension_check_precedes_zero_size(lib):
+    # an unsupported head dim is reported even when there is no work
+    assert call(B=0, d=80, ptrs=[0] * 8, lse=0) == A.ATTN_JVP_EUNSUPPORTED
+
+
+def test_fwd_rejects_bad_tensors_before_launch(lib):
+    import torch
+
+    q = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError):
+        A.fwd(q, q, q, q, q, q.transpose(2, 3))
+    with pytest.raises(TypeError):
+        A.fwd(*(torch.zeros(1, 1, 4, 64, dtype=torch.float16),) * 6)
+
+
+def test_no_device_returns_launch_error(lib):
+    """With no GPU present a well-formed call reports ELAUNCH instead of aborting."""
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this checks the no-device path only")
+    assert call() == A.ATTN_JVP_ELAUNCH
+    assert "HIP error" in A.attn_jvp_last_error()
+
+
+def test_ctypes_signature_is_c_abi(lib):
+    assert lib.attn_jvp_fwd.restype is ctypes.c_int
+    assert len(lib.attn_jvp_fwd.argtypes) == 17

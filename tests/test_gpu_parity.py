@@ -1,0 +1,170 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every test prints the case it runs before touching the GPU, so a failing run
+names its case.  Tolerances are the spec ones on O and tO (normalised
+max error <= 1e-5 for fp32, <= 2e-2 for bf16 against the oracle on the
+bf16-rounded inputs) and a relative bound on lse (see tests/_parity.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+from workloads import WORKLOADS, custom_workload, sample_rows
+
+from _parity import LSE_TOL, TOL, compare, device_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def A():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_forward_mode_attn_amd as A
+
+    A.load_library()
+    return A
+
+
+def run(A, w, stream=None):
+    x = device_inputs(w)
+    o, to, lse = A.fwd(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], scale=w.scale, stream=stream)
+    torch.cuda.synchronize()
+    return x, o, to, lse
+
+
+def check(w, res, per_head_gate=False):
+    tol = TOL[w.dtype]
+    print(f"  {w.name} B{w.B} H{w.H} Lq{w.Lq} Lk{w.Lk} d{w.d} {w.dtype}: "
+          f"O {res['O']:.3e} tO {res['tO']:.3e} lse {res['lse']:.3e}", flush=True)
+    assert res["O"] <= tol, res["O"]
+    assert res["tO"] <= tol, res["tO"]
+    assert res["lse"] <= LSE_TOL[w.dtype], res["lse"]
+    if per_head_gate:
+        worst = max(res["per_head"].items(), key=lambda kv: kv[1][1])
+        print(f"  worst per-head tO error {worst[1][1]:.3e} at (b, h) = {worst[0]}", flush=True)
+        assert worst[1][1] <= tol
+
+
+def test_tiny_self_fp32(A):
+    w = WORKLOADS["tiny_self_fp32"]
+    print(f"case {w.name}", flush=True)
+    _, o, to, lse = run(A, w)
+    check(w, compare(w, o, to, lse))
+
+
+RAGGED = [
+    # (B, H, Lq, Lk, d, dtype)
+    (1, 1, 1, 1, 64, "fp32"),
+    (1, 1, 1, 1, 128, "bf16"),
+    (1, 2, 129, 7, 128, "fp32"),
+    (2, 1, 65, 63, 64, "bf16"),
+    (1, 1, 300, 65, 128, "bf16"),
+    (1, 3, 130, 200, 64, "bf16"),
+    (1, 2, 257, 273, 128, "bf16"),
+    (2, 2, 383, 129, 128, "fp32"),
+    (1, 1, 128, 64, 128, "bf16"),
+    (1, 1, 64, 64, 64, "fp32"),
+    (1, 1, 17, 5000, 128, "bf16"),
+    (3, 5, 200, 96, 64, "fp32"),
+]
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,d,dtype", RAGGED)
+def test_ragged_shapes(A, B, H, Lq, Lk, d, dtype):
+    w = custom_workload(B, H, Lq, Lk, d, dtype, seed_id=2000 + Lq * 7 + Lk)
+    print(f"case ragged B{B} H{H} Lq{Lq} Lk{Lk} d{d} {dtype}", flush=True)
+    _, o, to, lse = run(A, w)
+    check(w, compare(w, o, to, lse))
+
+
+def test_image_self_bf16(A):
+    w = WORKLOADS["image_self_bf16"]
+    print(f"case {w.name} (all rows)", flush=True)
+    _, o, to, lse = run(A, w)
+    check(w, compare(w, o, to, lse), per_head_gate=True)
+
+
+def test_text_cross_bf16(A):
+    w = WORKLOADS["text_cross_bf16"]
+    print(f"case {w.name} (all rows)", flush=True)
+    _, o, to, lse = run(A, w)
+    check(w, compare(w, o, to, lse), per_head_gate=True)
+
+
+def test_video_self_bf16_sampled(A):
+    w = WORKLOADS["video_self_bf16"]
+    print(f"case {w.name} (256 sampled rows per head)", flush=True)
+    _, o, to, lse = run(A, w)
+    check(w, compare(w, o, to, lse, rows_fn=lambda b, h: sample_rows(w, b, h)), per_head_gate=True)
+
+
+def test_video_cross_stress_bf16_sampled(A):
+    w = WORKLOADS["video_cross_stress_bf16"]
+    print(f"case {w.name} (256 sampled rows per head)", flush=True)
+    _, o, to, lse = run(A, w)
+    check(w, compare(w, o, to, lse, rows_fn=lambda b, h: sample_rows(w, b, h)), per_head_gate=True)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64)])
+def test_outputs_fully_written_and_guard_bands(A, dtype, d):
+    """NaN-prefilled outputs must be fully overwritten; bytes around them untouched."""
+    w = custom_workload(1, 2, 201, 77, d, dtype, seed_id=3001)
+    print(f"case guard bands {dtype} d{d}", flush=True)
+    x = device_inputs(w)
+    tdt = x["q"].dtype
+    n = w.B * w.H * w.Lq * w.d
+    G = 4096
+    bufs = []
+    for _ in range(2):
+        full = torch.full((G + n + G,), 7.0, dtype=tdt, device="cuda")
+        full[G:G + n] = float("nan")
+        bufs.append(full)
+    lse_full = torch.full((G + w.B * w.H * w.Lq + G,), 7.0, dtype=torch.float32, device="cuda")
+    lse_full[G:-G] = float("nan")
+    o = bufs[0][G:G + n].view(w.B, w.H, w.Lq, w.d)
+    to = bufs[1][G:G + n].view(w.B, w.H, w.Lq, w.d)
+    lse = lse_full[G:-G].view(w.B, w.H, w.Lq)
+    A.fwd(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], scale=w.scale, out=(o, to, lse))
+    torch.cuda.synchronize()
+    for full in bufs + [lse_full]:
+        assert bool(torch.all(full[:G] == 7.0)) and bool(torch.all(full[-G:] == 7.0))
+        assert bool(torch.all(torch.isfinite(full[G:-G])))
+    check(w, compare(w, o, to, lse))
+
+
+def test_bitwise_deterministic_and_streams(A):
+    w = custom_workload(1, 4, 333, 1000, 128, "bf16", seed_id=3002)
+    print("case determinism", flush=True)
+    x = device_inputs(w)
+    r1 = A.fwd(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        r2 = A.fwd(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], stream=s)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.float32 else a.view(torch.int32),
+                           b.view(torch.uint8) if b.dtype != torch.float32 else b.view(torch.int32))
+
+
+def test_zero_size_is_noop(A):
+    print("case zero-size", flush=True)
+    assert A.attn_jvp_fwd(None, None, None, None, None, None, None, None, None,
+                          0, 4, 128, 128, 128, 0.1, A.ATTN_JVP_BF16) == A.ATTN_JVP_OK
+    assert A.attn_jvp_fwd(None, None, None, None, None, None, None, None, None,
+                          2, 4, 0, 128, 64, 0.1, A.ATTN_JVP_FP32) == A.ATTN_JVP_OK
+
+
+def test_tangent_along_values_gives_output(A):
+    """Invariant on the device: tangent (0, 0, V) makes tO equal O."""
+    w = custom_workload(1, 2, 150, 300, 128, "bf16", seed_id=3003)
+    print("case tangent (0,0,V)", flush=True)
+    x = device_inputs(w)
+    z = torch.zeros_like
+    o, to, _ = A.fwd(x["q"], x["k"], x["v"], z(x["q"]), z(x["k"]), x["v"])
+    torch.cuda.synchronize()
+    d = (o.float() - to.float()).abs().max().item() / o.float().abs().max().item()
+    print(f"  |tO - O| / max|O| = {d:.3e}", flush=True)
+    assert d <= 2e-2
+    assert np.isfinite(d)
