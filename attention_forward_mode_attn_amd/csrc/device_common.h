@@ -105,19 +105,22 @@ __device__ inline float tile_max_log2(const f32x16 (&s)[NB], float c) {
   return xhalf_max(mx) * c;
 }
 
-// Decide whether this tile moves the exponent base.  Returns true (wave-uniform)
-// when at least one row must rescale; alpha is then that row's factor (1 for the
-// others) and st.m has been updated.  st.l and st.a are rescaled here; the
-// caller rescales its matrix accumulators by alpha.
-__device__ inline bool update_max(RowState& st, float mt, float& alpha) {
+// Does this tile move the exponent base of any row of the wave?  (wave-uniform)
+__device__ inline bool needs_rescale(const RowState& st, float mt) {
+  return __builtin_amdgcn_ballot_w64(mt > st.m + kRescaleSlack) != 0;
+}
+
+// Move the exponent base of the rows that need it; returns each row's factor
+// (1 for the others) and rescales st.l and st.a.  The caller rescales its matrix
+// accumulators by the returned factor.
+__device__ inline float apply_rescale(RowState& st, float mt) {
   const bool need = mt > st.m + kRescaleSlack;
-  if (__builtin_amdgcn_ballot_w64(need) == 0) return false;
   const float m_new = need ? mt : st.m;
-  alpha = need ? fast_exp2(st.m - m_new) : 1.0f;
+  const float alpha = need ? fast_exp2(st.m - m_new) : 1.0f;
   st.m = m_new;
   st.l *= alpha;
   st.a *= alpha;
-  return true;
+  return alpha;
 }
 
 }  // namespace attnjvp

@@ -17,10 +17,11 @@
 //    Everything is transposed so that a lane owns one query: the softmax
 //    statistics are per-lane registers, and the S accumulator already has the
 //    layout of the P operand of the next products, so P never leaves registers;
-//  * K and tK tiles are copied to LDS row-major; V and tV are transposed on the
-//    way (4 keys x 8 dims per thread, v_perm_b32) into [dim][key] rows whose keys
-//    are permuted to match the accumulator layout, so every MFMA operand read is
-//    one 16-byte ds_read; 16-byte units are XOR-swizzled to avoid bank conflicts;
+//  * all four K/V tiles go global -> LDS by buffer_load ... lds (no staging
+//    registers; rows past Lk read as zero), row-major with XOR-swizzled
+//    16-byte units; K fragments are one ds_read_b128, V fragments are built by
+//    two ds_read_b64_tr_b16 transposing reads, whose 4-key runs match the
+//    accumulator layout of P, so V never needs an explicit transpose;
 //  * online softmax in the log2 domain with a lazily moved exponent base, per
 //    row running sums l = sum p and a = sum p*tS, and the epilogue
 //      O = acc_o / l,  tO = (acc_t - (a / l) acc_o) / l,  lse = (m + log2 l) ln 2.
@@ -52,106 +53,50 @@ struct Params {
 
 template <int D>
 struct Cfg {
-  static constexpr int kTileK = kBc * D * 2;        // bytes of one K (or tK) tile, [key][dim]
-  static constexpr int kTileV = D * kBc * 2;        // bytes of one V^T (or tV^T) tile, [dim][key]
-  static constexpr int kOffTK = kTileK;
-  static constexpr int kOffV = 2 * kTileK;
-  static constexpr int kOffTV = 2 * kTileK + kTileV;
-  static constexpr int kStage = 2 * kTileK + 2 * kTileV;
-  static constexpr int kKUnits = kBc * D / 8;       // 16-byte units in a K tile
-  static constexpr int kKPerThread = kKUnits / kThreads;
-  static constexpr int kVUnits = (kBc / 4) * (D / 8);  // (4 keys x 8 dims) units in a V tile
-  static constexpr int kVPerThread = 2 * kVUnits / kThreads;  // V and tV together
+  static constexpr int kRow = D * 2;               // bytes of one tile row (one key)
+  static constexpr int kTile = kBc * kRow;          // bytes of one K/tK/V/tV tile
+  static constexpr int kStage = 4 * kTile;          // K | tK | V | tV
+  static constexpr int kUnitsPerRow = kRow / 16;    // 16-byte units per row
+  static constexpr int kRowsPerLoad = 1024 / kRow;  // rows one 64-lane x 16-byte load fills
+  static constexpr int kLoadsPerWave = kTile / 1024 / kWaves;  // per tensor per tile
   static constexpr int kChunksD = D / 16;           // 16-wide head-dim chunks (S products)
   static constexpr int kBlocksD = D / 32;           // 32-row head-dim blocks (O products)
-  static_assert(kKUnits % kThreads == 0 && (2 * kVUnits) % kThreads == 0, "tile split");
+  static_assert(kTile % (1024 * kWaves) == 0, "tile split");
 };
 
-// Byte offset of 16-byte unit u of K-tile row r (row = one key).
+// LDS tile layout: row-major [key][dim], 16-byte units XOR-swizzled per row.
+//  * K, tK: unit u of key r sits at u ^ (r & 7).  The S products read one unit
+//    from each of 32 consecutive keys, so 8 consecutive lanes hit 8 distinct
+//    bank groups.
+//  * V, tV: unit u of key r sits at u ^ (2 * (r & 3)).  The O products read them
+//    with ds_read_b64_tr_b16: a 16-lane group reads 32 bytes from each of 4
+//    consecutive keys, which then land in 4 disjoint bank groups.
+__device__ inline int k_swz(int r) { return r & 7; }
+__device__ inline int v_swz(int r) { return 2 * (r & 3); }
+
+// Direct global->LDS copy of one tile: every wave-instruction fills 1 KB of LDS
+// in lane order (lane l -> bytes 16l..16l+15), so the swizzle is applied on the
+// global side by choosing which 16 bytes each lane fetches.  Rows past the end
+// of the tensor read as zero (buffer range check), so the last tile is padded
+// with zero keys.
 template <int D>
-__device__ inline uint32_t k_off(int r, int u) {
-  return r * (D * 2) + ((u ^ (r & 7)) << 4);
-}
-// Byte offset, in a V^T tile, of the 4-key group starting at permuted position
-// pos (a multiple of 4) in row d (row = one head-dim index, 64 keys = 128 bytes).
-__device__ inline uint32_t vt_off(int d, int pos) {
-  return d * (kBc * 2) + ((((pos >> 3) ^ (d & 7))) << 4) + (((pos >> 2) & 1) << 3);
-}
-// Keys 4g..4g+3 of a 16-key chunk are stored at these positions, so that
-// positions 8*hh .. 8*hh+7 hold the keys that accumulator registers 8*c'..8*c'+7
-// of half hh carry (see acc_row).
-__device__ inline int vt_pos(int g) {
-  const int gg = g & 3;
-  return 16 * (g >> 2) + (gg == 0 ? 0 : gg == 1 ? 8 : gg == 2 ? 4 : 12);
+__device__ inline uint32_t tile_load_voff(int blk, int lane, bool vswz) {
+  using C = Cfg<D>;
+  const int r = blk * C::kRowsPerLoad + lane / C::kUnitsPerRow;
+  const int pu = lane % C::kUnitsPerRow;
+  const int u = pu ^ (vswz ? v_swz(r) : k_swz(r));
+  return (uint32_t)(r * C::kRow + u * 16);
 }
 
-template <int D>
-struct Staging {
-  u32x4 k[Cfg<D>::kKPerThread];
-  u32x4 tk[Cfg<D>::kKPerThread];
-  u32x4 v[Cfg<D>::kVPerThread][4];
-};
-
-// V-unit z (over V then tV) -> (tensor, key group g, dim octet o).
-template <int D>
-__device__ inline void v_unit(int z, int& tensor, int& g, int& o) {
-  tensor = z / Cfg<D>::kVUnits;
-  const int zz = z % Cfg<D>::kVUnits;
-  g = zz % (kBc / 4);
-  o = zz / (kBc / 4);
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
-template <int D>
-__device__ inline void issue_tile_loads(Staging<D>& sg, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rtk,
-                                        __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rtv, int key0, int t) {
-#pragma unroll
-  for (int i = 0; i < Cfg<D>::kKPerThread; ++i) {
-    const int e = t + kThreads * i;
-    const int r = e / (D / 8), u = e % (D / 8);
-    const uint32_t off = ((key0 + r) * D + u * 8) * 2;
-    sg.k[i] = buf_load16(rk, off);
-    sg.tk[i] = buf_load16(rtk, off);
-  }
-#pragma unroll
-  for (int i = 0; i < Cfg<D>::kVPerThread; ++i) {
-    int tensor, g, o;
-    v_unit<D>(t + kThreads * i, tensor, g, o);
-    // tensor is uniform over each wave (it depends on i and on the wave index only)
-    tensor = __builtin_amdgcn_readfirstlane(tensor);
-    const __amdgpu_buffer_rsrc_t r = tensor ? rtv : rv;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sg.v[i][j] = buf_load16(r, ((key0 + 4 * g + j) * D + 8 * o) * 2);
-  }
-}
-
-template <int D>
-__device__ inline void store_tile(const Staging<D>& sg, char* stage, int t) {
-#pragma unroll
-  for (int i = 0; i < Cfg<D>::kKPerThread; ++i) {
-    const int e = t + kThreads * i;
-    const int r = e / (D / 8), u = e % (D / 8);
-    *reinterpret_cast<u32x4*>(stage + k_off<D>(r, u)) = sg.k[i];
-    *reinterpret_cast<u32x4*>(stage + Cfg<D>::kOffTK + k_off<D>(r, u)) = sg.tk[i];
-  }
-#pragma unroll
-  for (int i = 0; i < Cfg<D>::kVPerThread; ++i) {
-    int tensor, g, o;
-    v_unit<D>(t + kThreads * i, tensor, g, o);
-    char* base = stage + Cfg<D>::kOffV + tensor * Cfg<D>::kTileV;
-    const int pos = vt_pos(g);
-    const u32x4 &r0 = sg.v[i][0], &r1 = sg.v[i][1], &r2 = sg.v[i][2], &r3 = sg.v[i][3];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // dword w of a row holds dims 8o+2w (low half) and 8o+2w+1 (high half)
-      u32x2 lo, hi;
-      lo[0] = __builtin_amdgcn_perm(r1[w], r0[w], 0x05040100u);
-      lo[1] = __builtin_amdgcn_perm(r3[w], r2[w], 0x05040100u);
-      hi[0] = __builtin_amdgcn_perm(r1[w], r0[w], 0x07060302u);
-      hi[1] = __builtin_amdgcn_perm(r3[w], r2[w], 0x07060302u);
-      *reinterpret_cast<u32x2*>(base + vt_off(8 * o + 2 * w, pos)) = lo;
-      *reinterpret_cast<u32x2*>(base + vt_off(8 * o + 2 * w + 1, pos)) = hi;
-    }
-  }
+// LDS read helpers.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ inline i16x4 lds_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(__attribute__((address_space(3))) const char*)p);
 }
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
@@ -169,22 +114,21 @@ template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_jvp_bf16_kernel(Params p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kStage];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStage];
 
   const int t = threadIdx.x;
-  const int lane = t & 63, wv = t >> 6, n = lane & 31, hh = lane >> 5;
+  const int lane = t & 63, n = lane & 31, hh = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
   const int blk = xcd_logical_block(blockIdx.x, p.n_blocks);
   const int bh = blk / p.n_qtiles, qt = blk % p.n_qtiles;
   const int Lq = p.Lq, Lk = p.Lk;
 
   const size_t qhead = (size_t)bh * Lq * D * 2, khead = (size_t)bh * Lk * D * 2;
-  const uint32_t qbytes = (uint32_t)Lq * D * 2, kbytes = (uint32_t)Lk * D * 2;
+  const uint32_t qbytes = (uint32_t)Lq * D * 2;
   const auto rq = make_rsrc((const char*)p.q + qhead, qbytes);
   const auto rtq = make_rsrc((const char*)p.tq + qhead, qbytes);
-  const auto rk = make_rsrc((const char*)p.k + khead, kbytes);
-  const auto rtk = make_rsrc((const char*)p.tk + khead, kbytes);
-  const auto rv = make_rsrc((const char*)p.v + khead, kbytes);
-  const auto rtv = make_rsrc((const char*)p.tv + khead, kbytes);
+  const char* kbase[4] = {(const char*)p.k + khead, (const char*)p.tk + khead,
+                          (const char*)p.v + khead, (const char*)p.tv + khead};
 
   // Q and tQ fragments (B operand of S^T = K Q^T): lane (n, hh) holds dims
   // 16c + 8hh .. +7 of its query row.  Rows past Lq read as zero.
@@ -207,51 +151,45 @@ void attn_jvp_bf16_kernel(Params p) {
   const float scale = p.scale;
   const float c2 = scale * kLog2e;
 
-  // Per-lane LDS read offsets (the swizzle term is n & 7 for every read).
-  const int sw = n & 7;
-  const uint32_t krow_off = n * (D * 2);   // + 32*kb*(D*2)
-  const uint32_t vrow_off = n * (kBc * 2); // + 32*b*(kBc*2)
-
-  const int nt = (Lk + kBc - 1) / kBc;
-  Staging<D> sg;
-  issue_tile_loads<D>(sg, rk, rtk, rv, rtv, 0, t);
-  store_tile<D>(sg, smem, t);
-  __syncthreads();
-
-  for (int j = 0; j < nt; ++j) {
-    const char* cur = smem + (j & 1) * C::kStage;
-    if (j + 1 < nt) issue_tile_loads<D>(sg, rk, rtk, rv, rtv, (j + 1) * kBc, t);
-
-    // ---- logits and tangent logits --------------------------------------
-    f32x16 s[2] = {f32x16{}, f32x16{}}, ts[2] = {f32x16{}, f32x16{}};
+  // Per-lane global offsets of this wave's share of a tile copy (loop invariant).
+  uint32_t voff_k[C::kLoadsPerWave], voff_v[C::kLoadsPerWave];
 #pragma unroll
-    for (int c = 0; c < C::kChunksD; ++c) {
-      const uint32_t u = ((2 * c + hh) ^ sw) << 4;
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(cur + krow_off + u);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(cur + krow_off + 32 * D * 2 + u);
-      const bf16x8 tk0 = *reinterpret_cast<const bf16x8*>(cur + C::kOffTK + krow_off + u);
-      const bf16x8 tk1 = *reinterpret_cast<const bf16x8*>(cur + C::kOffTK + krow_off + 32 * D * 2 + u);
-      s[0] = mfma(k0, qf[c], s[0]);
-      s[1] = mfma(k1, qf[c], s[1]);
-      ts[0] = mfma(k0, tqf[c], ts[0]);
-      ts[1] = mfma(k1, tqf[c], ts[1]);
-      ts[0] = mfma(tk0, qf[c], ts[0]);
-      ts[1] = mfma(tk1, qf[c], ts[1]);
-    }
-
-    // ---- online softmax --------------------------------------------------
-    if (j == nt - 1 && (Lk % kBc) != 0) mask_tail<2>(s, Lk - j * kBc, hh);
-    float alpha;
-    if (update_max(st, tile_max_log2<2>(s, c2), alpha)) {
+  for (int i = 0; i < C::kLoadsPerWave; ++i) {
+    voff_k[i] = tile_load_voff<D>(wv * C::kLoadsPerWave + i, lane, false);
+    voff_v[i] = tile_load_voff<D>(wv * C::kLoadsPerWave + i, lane, true);
+  }
+  auto issue_tile = [&](int j) {
+    const int key0 = j * kBc;
+    const uint32_t left = (uint32_t)(Lk - key0) * D * 2;
+    char* stage = smem + (j & 1) * C::kStage;
 #pragma unroll
-      for (int b = 0; b < C::kBlocksD; ++b) {
-        acc_o[b] *= alpha;
-        acc_t[b] *= alpha;
-      }
+    for (int tn = 0; tn < 4; ++tn) {
+      const auto r = make_rsrc(kbase[tn] + (size_t)key0 * D * 2, left);
+#pragma unroll
+      for (int i = 0; i < C::kLoadsPerWave; ++i)
+        lds_dma16(r, stage + tn * C::kTile + (wv * C::kLoadsPerWave + i) * 1024, tn < 2 ? voff_k[i] : voff_v[i]);
     }
-    // P and P*tS as bf16 B operands: chunk cc (keys 16cc..16cc+15) is
-    // registers 8*(cc%2) .. +7 of key block cc/2.
-    bf16x8 pf[4], ptf[4];
+  };
+
+  // Per-lane LDS read offsets.
+  // K fragment (key block kb, dim chunk c): key 32kb + n, unit (2c + hh) ^ (n & 7).
+  const uint32_t krow = n * C::kRow;
+  const int ksw = n & 7;
+  // V fragment via ds_read_b64_tr_b16: in 16-lane group G = lane / 16 (half
+  // hh = G / 2, dims 16(G & 1) .. +15 of the 32-dim block), source lane s reads
+  // 4 dims starting at 4(s & 3) of key 4hh + (s >> 2) (+ 16cc + 8rho).
+  const int G = lane >> 4, sl = lane & 15;
+  const int vkey = 4 * (G >> 1) + (sl >> 2);
+  uint32_t voff_tr[C::kBlocksD];
+#pragma unroll
+  for (int b = 0; b < C::kBlocksD; ++b) {
+    const int d0 = 32 * b + 16 * (G & 1) + 4 * (sl & 3);
+    voff_tr[b] = vkey * C::kRow + ((((d0 >> 3) ^ v_swz(vkey)) << 4) | ((d0 & 7) * 2));
+  }
+
+  // P and P*tS of one tile as bf16 B operands, accumulated into l and a:
+  // chunk cc (keys 16cc..16cc+15) is registers 8*(cc%2) .. +7 of key block cc/2.
+  auto probabilities = [&](const f32x16 (&s)[2], const f32x16 (&ts)[2], bf16x8 (&pf)[4], bf16x8 (&ptf)[4]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -270,24 +208,91 @@ void attn_jvp_bf16_kernel(Params p) {
         ptf[cc][i + 1] = __builtin_bit_cast(bf16x2, qq)[1];
       }
     }
-
-    // ---- O and tO products ---------------------------------------------
+  };
+  // O^T += V^T P^T and tO^T += tV^T P^T + V^T (P*tS)^T for one tile.  The V^T
+  // fragment (dim block b, key chunk cc) has keys 16cc + 4hh + 0..3 in elements
+  // 0..3 and 16cc + 8 + 4hh + 0..3 in elements 4..7, matching the P registers.
+  auto accumulate = [&](const char* cur, const bf16x8 (&pf)[4], const bf16x8 (&ptf)[4]) {
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      const uint32_t u = ((2 * cc + hh) ^ sw) << 4;
+      bf16x8 vv[C::kBlocksD];
 #pragma unroll
       for (int b = 0; b < C::kBlocksD; ++b) {
-        const uint32_t off = vrow_off + 32 * b * (kBc * 2) + u;
-        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(cur + C::kOffV + off);
-        const bf16x8 tvv = *reinterpret_cast<const bf16x8*>(cur + C::kOffTV + off);
-        acc_o[b] = mfma(vv, pf[cc], acc_o[b]);
+        const char* vb = cur + 2 * C::kTile + 16 * cc * C::kRow + voff_tr[b];
+        const i16x4 lo = lds_tr16(vb), hi = lds_tr16(vb + 8 * C::kRow);
+        const char* tb = vb + C::kTile;
+        const i16x4 tlo = lds_tr16(tb), thi = lds_tr16(tb + 8 * C::kRow);
+        vv[b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const bf16x8 tvv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc_o[b] = mfma(vv[b], pf[cc], acc_o[b]);
         acc_t[b] = mfma(tvv, pf[cc], acc_t[b]);
-        acc_t[b] = mfma(vv, ptf[cc], acc_t[b]);
       }
+#pragma unroll
+      for (int b = 0; b < C::kBlocksD; ++b) acc_t[b] = mfma(vv[b], ptf[cc], acc_t[b]);
     }
+  };
 
-    if (j + 1 < nt) store_tile<D>(sg, smem + ((j + 1) & 1) * C::kStage, t);
-    __syncthreads();
+  const int nt = (Lk + kBc - 1) / kBc;
+  issue_tile(0);
+  int j = 0;
+  f32x16 s[2], ts[2];
+  float mt = 0.0f;
+  // The hot loop only feeds the accumulators to MFMAs.  A tile whose row max
+  // moves the exponent base (always the first, rarely a later one) leaves the
+  // loop, rescales the accumulators outside it and re-enters.
+  while (true) {
+    bool rescale = false;
+    for (; j < nt; ++j) {
+      // the tile j copy must have landed for every wave before it is read
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      const char* cur = smem + (j & 1) * C::kStage;
+      if (j + 1 < nt) issue_tile(j + 1);
+
+      // ---- logits and tangent logits ------------------------------------
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        ts[kb] = f32x16{};
+      }
+#pragma unroll
+      for (int c = 0; c < C::kChunksD; ++c) {
+        const uint32_t u = krow + (((2 * c + hh) ^ ksw) << 4);
+        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(cur + u);
+        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(cur + 32 * C::kRow + u);
+        const bf16x8 tk0 = *reinterpret_cast<const bf16x8*>(cur + C::kTile + u);
+        const bf16x8 tk1 = *reinterpret_cast<const bf16x8*>(cur + C::kTile + 32 * C::kRow + u);
+        s[0] = mfma(k0, qf[c], s[0]);
+        s[1] = mfma(k1, qf[c], s[1]);
+        ts[0] = mfma(k0, tqf[c], ts[0]);
+        ts[1] = mfma(k1, tqf[c], ts[1]);
+        ts[0] = mfma(tk0, qf[c], ts[0]);
+        ts[1] = mfma(tk1, qf[c], ts[1]);
+      }
+
+      // ---- online softmax ------------------------------------------------
+      if (j == nt - 1 && (Lk % kBc) != 0) mask_tail<2>(s, Lk - j * kBc, hh);
+      mt = tile_max_log2<2>(s, c2);
+      if (needs_rescale(st, mt)) {
+        rescale = true;
+        break;
+      }
+      bf16x8 pf[4], ptf[4];
+      probabilities(s, ts, pf, ptf);
+      accumulate(cur, pf, ptf);
+    }
+    if (!rescale) break;
+    // ---- tile j with a new exponent base ----------------------------------
+    const float alpha = apply_rescale(st, mt);
+#pragma unroll
+    for (int b = 0; b < C::kBlocksD; ++b) {
+      acc_o[b] *= alpha;
+      acc_t[b] *= alpha;
+    }
+    bf16x8 pf[4], ptf[4];
+    probabilities(s, ts, pf, ptf);
+    accumulate(smem + (j & 1) * C::kStage, pf, ptf);
+    ++j;
   }
 
   // ---- epilogue ------------------------------------------------------------

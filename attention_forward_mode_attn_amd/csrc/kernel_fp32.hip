@@ -127,49 +127,18 @@ void attn_jvp_fp32_kernel(Params p) {
   const float c2 = scale * kLog2e;
   const int sw = n & 7;
 
-  const int nt = (Lk + kBcF - 1) / kBcF;
-  Staging<D> sg;
-  issue_tile_loads<D>(sg, rkv, 0, t);
-  store_tile<D>(sg, smem, t);
-  __syncthreads();
-
-  for (int j = 0; j < nt; ++j) {
-    const char* cur = smem + (j & 1) * C::kStage;
-    if (j + 1 < nt) issue_tile_loads<D>(sg, rkv, (j + 1) * kBcF, t);
-
-    f32x16 s[1] = {f32x16{}}, ts[1] = {f32x16{}};
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-      // unit hh*D/8 + i of row n holds dims hh*D/2 + 4i .. +3
-      const uint32_t off = n * (D * 4) + (((hh * (D / 8) + i) ^ sw) << 4);
-      const f32x4 kk = *reinterpret_cast<const f32x4*>(cur + off);
-      const f32x4 tkk = *reinterpret_cast<const f32x4*>(cur + C::kTile + off);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[0] = mfma(kk[e], qf[4 * i + e], s[0]);
-        ts[0] = mfma(kk[e], tqf[4 * i + e], ts[0]);
-        ts[0] = mfma(tkk[e], qf[4 * i + e], ts[0]);
-      }
-    }
-
-    if (j == nt - 1 && (Lk % kBcF) != 0) mask_tail<1>(s, Lk - j * kBcF, hh);
-    float alpha;
-    if (update_max(st, tile_max_log2<1>(s, c2), alpha)) {
-#pragma unroll
-      for (int b = 0; b < C::kBlocksD; ++b) {
-        acc_o[b] *= alpha;
-        acc_t[b] *= alpha;
-      }
-    }
-    float pv[16], ptv[16];
+  // P and P*tS of one tile (fp32, straight from the S accumulator), and the
+  // O / tO products: MFMA r pairs the keys that register r holds in the two halves.
+  auto probabilities = [&](const f32x16& s, const f32x16& ts, float (&pv)[16], float (&ptv)[16]) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      pv[r] = fast_exp2(__builtin_fmaf(s[0][r], c2, -st.m));
-      ptv[r] = pv[r] * (ts[0][r] * scale);
+      pv[r] = fast_exp2(__builtin_fmaf(s[r], c2, -st.m));
+      ptv[r] = pv[r] * (ts[r] * scale);
       st.l += pv[r];
       st.a += ptv[r];
     }
-
+  };
+  auto accumulate = [&](const char* cur, const float (&pv)[16], const float (&ptv)[16]) {
     const char* vbase = cur + 2 * C::kTile;
     const char* tvbase = cur + 3 * C::kTile;
 #pragma unroll
@@ -185,9 +154,71 @@ void attn_jvp_fp32_kernel(Params p) {
         acc_t[b] = mfma(vv, ptv[r], acc_t[b]);
       }
     }
+  };
 
+  const int nt = (Lk + kBcF - 1) / kBcF;
+  Staging<D> sg;
+  issue_tile_loads<D>(sg, rkv, 0, t);
+  store_tile<D>(sg, smem, t);
+  __syncthreads();
+  int j = 0;
+  f32x16 s, ts;
+  float mt = 0.0f;
+  // Same structure as the bf16 kernel: tiles that move the exponent base leave
+  // the hot loop so that the accumulators are rescaled outside it.
+  while (true) {
+    bool rescale = false;
+    for (; j < nt; ++j) {
+      const char* cur = smem + (j & 1) * C::kStage;
+      if (j + 1 < nt) issue_tile_loads<D>(sg, rkv, (j + 1) * kBcF, t);
+
+      s = f32x16{};
+      ts = f32x16{};
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        // unit hh*D/8 + i of row n holds dims hh*D/2 + 4i .. +3
+        const uint32_t off = n * (D * 4) + (((hh * (D / 8) + i) ^ sw) << 4);
+        const f32x4 kk = *reinterpret_cast<const f32x4*>(cur + off);
+        const f32x4 tkk = *reinterpret_cast<const f32x4*>(cur + C::kTile + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s = mfma(kk[e], qf[4 * i + e], s);
+          ts = mfma(kk[e], tqf[4 * i + e], ts);
+          ts = mfma(tkk[e], qf[4 * i + e], ts);
+        }
+      }
+      if (j == nt - 1 && (Lk % kBcF) != 0) {
+        f32x16 sm[1] = {s};
+        mask_tail<1>(sm, Lk - j * kBcF, hh);
+        s = sm[0];
+      }
+      {
+        const f32x16 sm[1] = {s};
+        mt = tile_max_log2<1>(sm, c2);
+      }
+      if (needs_rescale(st, mt)) {
+        rescale = true;
+        break;
+      }
+      float pv[16], ptv[16];
+      probabilities(s, ts, pv, ptv);
+      accumulate(cur, pv, ptv);
+      if (j + 1 < nt) store_tile<D>(sg, smem + ((j + 1) & 1) * C::kStage, t);
+      __syncthreads();
+    }
+    if (!rescale) break;
+    const float alpha = apply_rescale(st, mt);
+#pragma unroll
+    for (int b = 0; b < C::kBlocksD; ++b) {
+      acc_o[b] *= alpha;
+      acc_t[b] *= alpha;
+    }
+    float pv[16], ptv[16];
+    probabilities(s, ts, pv, ptv);
+    accumulate(smem + (j & 1) * C::kStage, pv, ptv);
     if (j + 1 < nt) store_tile<D>(sg, smem + ((j + 1) & 1) * C::kStage, t);
     __syncthreads();
+    ++j;
   }
 
   const float l = xhalf_sum(st.l), a = xhalf_sum(st.a);

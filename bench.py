@@ -1,0 +1,217 @@
+"""Benchmark: attention forward + JVP throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one attn_jvp_fwd call over the whole workload (inputs resident in
+HBM, outputs preallocated).  The default workload is the 32760-token video
+self-attention layer (B=1, H=40, Lq=Lk=32760, d=128, bf16).  Throughput counts
+the nominal 12*B*H*Lq*Lk*d flops of the six dense products.  Prints ONE JSON
+line on stdout.
+
+Extra modes used by the profiling recipes:
+  --copy-calibration   time/profile a plain device copy of known size (HBM
+                       counter calibration) instead of the kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix/vector, vendor figure
+METRIC = "attention-JVP TFLOP/s (12*B*H*Lq*Lk*d) + % bf16 MFMA peak, 1 MI355X"
+KERNEL_SOURCES = ["attention_forward_mode_attn_amd/csrc/kernel_bf16.hip",
+                  "attention_forward_mode_attn_amd/csrc/kernel_fp32.hip",
+                  "attention_forward_mode_attn_amd/csrc/device_common.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None
+    when there is none for this workload or the kernel changed since."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_src or not m_b or m_src.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(w, budget_s: float = 20.0):
+    """Time the fp64 oracle on sampled query rows of the same workload."""
+    import numpy as np
+
+    from oracle import attention_jvp_head
+    from workloads import TENSORS, head_array, sample_rows
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max((int(x.get("num_threads", 1)) for x in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    rows_done = 0
+    t_total = 0.0
+    heads = 0
+    for b in range(w.B):
+        for h in range(w.H):
+            a = {t: head_array(w, t, b, h) for t in TENSORS}
+            rows = sample_rows(w, b, h)
+            t0 = time.perf_counter()
+            attention_jvp_head(a["q"], a["k"], a["v"], a["tq"], a["tk"], a["tv"], w.scale, rows=rows)
+            t_total += time.perf_counter() - t0
+            rows_done += rows.size
+            heads += 1
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    flops = 12.0 * rows_done * w.Lk * w.d
+    full_s = t_total / rows_done * (w.B * w.H * w.Lq)
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{rows_done} query rows ({rows.size} per head x {heads} heads) of {w.name}, "
+                  f"all {w.Lk} keys; {t_total:.1f} s; full workload extrapolates to {full_s:.0f} s",
+        "float": "f64",
+        "_np": np.__version__,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="video_self_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the attention JVP shards by (batch, head) with no exchange: run one process per GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_forward_mode_attn_amd as A
+    from workloads import WORKLOADS
+
+    from workloads.device import device_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": args.warmup + args.steps}))
+        return
+
+    w = WORKLOADS[args.workload]
+    print(f"bench: {w.name} B{w.B} H{w.H} Lq{w.Lq} Lk{w.Lk} d{w.d} {w.dtype}: generating inputs",
+          file=sys.stderr, flush=True)
+    x = device_inputs(w)
+    o = torch.empty_like(x["q"])
+    to = torch.empty_like(x["q"])
+    lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        A.fwd(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], scale=w.scale, out=(o, to, lse), stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    per = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for a, b in per:
+        a.record(stream)
+        step()
+        b.record(stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = ev0.elapsed_time(ev1)
+    launch_ms = sorted(a.elapsed_time(b) for a, b in per)
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    ms_per_step = total_ms / args.steps
+
+    flops = w.flops
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": measured_traffic(w.name),
+        "kernel": "attn_jvp_bf16_kernel<128>" if w.dtype == "bf16" else f"attn_jvp_fp32_kernel<{w.d}>",
+        "avg_launch_ms": round(avg_launch_ms, 4),
+        "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4),
+        "min_launch_ms": round(launch_ms[0], 4),
+        "algorithmic_flops_per_launch": flops,
+        "algorithmic_bytes_per_launch": w.algorithmic_bytes,
+    }
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "d": w.d,
+                   "scale": w.scale, "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "wall_s_timed_region": round(wall, 3),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the fp64 oracle on sampled rows (cpu_baseline)", file=sys.stderr, flush=True)
+        cb = cpu_baseline(w, args.cpu_budget)
+        cb.pop("_np", None)
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -10,7 +10,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 from oracle import attention_jvp_head
-from workloads import TENSORS, head_array, head_upload
+from workloads import TENSORS, head_array
+from workloads.device import device_inputs  # noqa: F401  (re-exported for the tests)
 
 # Spec tolerances on O and tO: normalised max error max|x - ref| / max|ref|.
 TOL = {"fp32": 1e-5, "bf16": 2e-2}
@@ -30,32 +31,6 @@ def lse_err(x, ref) -> float:
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     return float(np.max(np.abs(x - ref) / np.maximum(1.0, np.abs(ref)))) if ref.size else 0.0
-
-
-def torch_dtype(w):
-    import torch
-
-    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
-
-
-def device_inputs(w, device="cuda", threads=8):
-    """Allocate the six inputs on the device and fill them head by head."""
-    import torch
-
-    tdt = torch_dtype(w)
-    out = {t: torch.empty(w.shape(t), dtype=tdt, device=device) for t in TENSORS}
-    jobs = [(t, b, h) for t in TENSORS for b in range(w.B) for h in range(w.H)]
-
-    def gen(job):
-        t, b, h = job
-        return job, head_upload(w, t, b, h)
-
-    with ThreadPoolExecutor(threads) as ex:
-        for (t, b, h), arr in ex.map(gen, jobs):
-            src = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16" \
-                else torch.from_numpy(arr)
-            out[t][b, h].copy_(src)
-    return out
 
 
 def oracle_head(w, b, h, rows=None):
