@@ -65,14 +65,21 @@ struct Cfg {
 };
 
 // LDS tile layout: row-major [key][dim], 16-byte units XOR-swizzled per row.
-//  * K, tK: unit u of key r sits at u ^ (r & 7).  The S products read one unit
-//    from each of 32 consecutive keys, so 8 consecutive lanes hit 8 distinct
-//    bank groups.
-//  * V, tV: unit u of key r sits at u ^ (2 * (r & 3)).  The O products read them
-//    with ds_read_b64_tr_b16: a 16-lane group reads 32 bytes from each of 4
-//    consecutive keys, which then land in 4 disjoint bank groups.
-__device__ inline int k_swz(int r) { return r & 7; }
-__device__ inline int v_swz(int r) { return 2 * (r & 3); }
+// gfx950 LDS has 64 banks (256 bytes per cycle); a 16-byte read is served 16
+// lanes at a time, a ds_read_b64_tr_b16 32 lanes at a time.
+//  * K, tK: the S products read unit u of 32 consecutive keys; the swizzle
+//    spreads any 16 consecutive keys over all 16 bank groups (d = 128: rows are
+//    256 bytes, unit ^ (key & 15); d = 64: rows are 128 bytes, two per bank
+//    window, unit ^ ((key >> 1) & 7)).
+//  * V, tV: a 32-lane half of a transposing read takes 64 bytes from each of 4
+//    consecutive keys; the swizzle moves each key's 4-unit group to its own
+//    quarter of the bank window (d = 128: unit ^ 4(key & 3); d = 64: two keys
+//    per window, unit ^ 4((key >> 1) & 1)).
+// Both layouts were checked conflict-free with the SQ_LDS_BANK_CONFLICT counter.
+template <int D>
+__device__ inline int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ inline int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 // Direct global->LDS copy of one tile: every wave-instruction fills 1 KB of LDS
 // in lane order (lane l -> bytes 16l..16l+15), so the swizzle is applied on the
@@ -84,7 +91,7 @@ __device__ inline uint32_t tile_load_voff(int blk, int lane, bool vswz) {
   using C = Cfg<D>;
   const int r = blk * C::kRowsPerLoad + lane / C::kUnitsPerRow;
   const int pu = lane % C::kUnitsPerRow;
-  const int u = pu ^ (vswz ? v_swz(r) : k_swz(r));
+  const int u = pu ^ (vswz ? v_swz<D>(r) : k_swz<D>(r));
   return (uint32_t)(r * C::kRow + u * 16);
 }
 
@@ -158,12 +165,15 @@ void attn_jvp_bf16_kernel(Params p) {
     voff_k[i] = tile_load_voff<D>(wv * C::kLoadsPerWave + i, lane, false);
     voff_v[i] = tile_load_voff<D>(wv * C::kLoadsPerWave + i, lane, true);
   }
-  auto issue_tile = [&](int j) {
+  // LDS stage s holds K | tK | V | tV.  K/tK of tile j and V/tV of tile j live in
+  // stage j & 1; the K half is fetched two tiles ahead, the V half one tile
+  // ahead.  Tiles at or past the end are fetched as zeros (empty range).
+  auto issue = [&](int j, int tn0) {
     const int key0 = j * kBc;
-    const uint32_t left = (uint32_t)(Lk - key0) * D * 2;
+    const uint32_t left = key0 < Lk ? (uint32_t)(Lk - key0) * D * 2 : 0u;
     char* stage = smem + (j & 1) * C::kStage;
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
+    for (int tn = tn0; tn < tn0 + 2; ++tn) {
       const auto r = make_rsrc(kbase[tn] + (size_t)key0 * D * 2, left);
 #pragma unroll
       for (int i = 0; i < C::kLoadsPerWave; ++i)
@@ -172,9 +182,9 @@ void attn_jvp_bf16_kernel(Params p) {
   };
 
   // Per-lane LDS read offsets.
-  // K fragment (key block kb, dim chunk c): key 32kb + n, unit (2c + hh) ^ (n & 7).
+  // K fragment (key block kb, dim chunk c): key 32kb + n, unit (2c + hh) ^ k_swz(n).
   const uint32_t krow = n * C::kRow;
-  const int ksw = n & 7;
+  const int ksw = k_swz<D>(n);
   // V fragment via ds_read_b64_tr_b16: in 16-lane group G = lane / 16 (half
   // hh = G / 2, dims 16(G & 1) .. +15 of the 32-dim block), source lane s reads
   // 4 dims starting at 4(s & 3) of key 4hh + (s >> 2) (+ 16cc + 8rho).
@@ -184,8 +194,32 @@ void attn_jvp_bf16_kernel(Params p) {
 #pragma unroll
   for (int b = 0; b < C::kBlocksD; ++b) {
     const int d0 = 32 * b + 16 * (G & 1) + 4 * (sl & 3);
-    voff_tr[b] = vkey * C::kRow + ((((d0 >> 3) ^ v_swz(vkey)) << 4) | ((d0 & 7) * 2));
+    voff_tr[b] = vkey * C::kRow + ((((d0 >> 3) ^ v_swz<D>(vkey)) << 4) | ((d0 & 7) * 2));
   }
+
+  // S^T = K Q^T and tS^T = K tQ^T + tK Q^T of tile j (K half of stage j & 1).
+  auto logits = [&](int j, f32x16 (&s)[2], f32x16 (&ts)[2]) {
+    const char* cur = smem + (j & 1) * C::kStage;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      ts[kb] = f32x16{};
+    }
+#pragma unroll
+    for (int c = 0; c < C::kChunksD; ++c) {
+      const uint32_t u = krow + (((2 * c + hh) ^ ksw) << 4);
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(cur + u);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(cur + 32 * C::kRow + u);
+      const bf16x8 tk0 = *reinterpret_cast<const bf16x8*>(cur + C::kTile + u);
+      const bf16x8 tk1 = *reinterpret_cast<const bf16x8*>(cur + C::kTile + 32 * C::kRow + u);
+      s[0] = mfma(k0, qf[c], s[0]);
+      s[1] = mfma(k1, qf[c], s[1]);
+      ts[0] = mfma(k0, tqf[c], ts[0]);
+      ts[1] = mfma(k1, tqf[c], ts[1]);
+      ts[0] = mfma(tk0, qf[c], ts[0]);
+      ts[1] = mfma(tk1, qf[c], ts[1]);
+    }
+  };
 
   // P and P*tS of one tile as bf16 B operands, accumulated into l and a:
   // chunk cc (keys 16cc..16cc+15) is registers 8*(cc%2) .. +7 of key block cc/2.
@@ -209,10 +243,11 @@ void attn_jvp_bf16_kernel(Params p) {
       }
     }
   };
-  // O^T += V^T P^T and tO^T += tV^T P^T + V^T (P*tS)^T for one tile.  The V^T
+  // O^T += V^T P^T and tO^T += tV^T P^T + V^T (P*tS)^T for tile j.  The V^T
   // fragment (dim block b, key chunk cc) has keys 16cc + 4hh + 0..3 in elements
   // 0..3 and 16cc + 8 + 4hh + 0..3 in elements 4..7, matching the P registers.
-  auto accumulate = [&](const char* cur, const bf16x8 (&pf)[4], const bf16x8 (&ptf)[4]) {
+  auto accumulate = [&](int j, const bf16x8 (&pf)[4], const bf16x8 (&ptf)[4]) {
+    const char* cur = smem + (j & 1) * C::kStage;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
       bf16x8 vv[C::kBlocksD];
@@ -233,66 +268,81 @@ void attn_jvp_bf16_kernel(Params p) {
   };
 
   const int nt = (Lk + kBc - 1) / kBc;
-  issue_tile(0);
+  const bool ragged = (Lk % kBc) != 0;
+  f32x16 s[2], ts[2];    // logits of the tile whose probabilities come next
+  f32x16 sn[2], tsn[2];  // logits of the following tile, being accumulated
+
+  // Prologue: tile 0 logits; its max sets the exponent base.
+  issue(0, 0);
+  issue(0, 2);
+  issue(1, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): all DMA of this wave landed
+  __syncthreads();
+  logits(0, s, ts);
+  if (nt == 1 && ragged) mask_tail<2>(s, Lk, hh);
+  float mt = tile_max_log2<2>(s, c2);
+  apply_rescale(st, mt);  // accumulators are still zero
+  __syncthreads();        // every wave is done with K of tile 0 before it is refilled
+
+  // Iteration j: probabilities of tile j while the logits of tile j + 1 are
+  // computed, then the O / tO products of tile j while the max of tile j + 1 is
+  // reduced.  In flight meanwhile: K of tile j + 2 and V of tile j + 1.
+  auto iteration = [&](int j, bool mask_next) {
+    issue(j + 2, 0);
+    issue(j + 1, 2);
+    bf16x8 pf[4], ptf[4];
+    probabilities(s, ts, pf, ptf);
+    logits(j + 1, sn, tsn);
+    accumulate(j, pf, ptf);
+    if (mask_next) mask_tail<2>(sn, Lk - (j + 1) * kBc, hh);
+    mt = tile_max_log2<2>(sn, c2);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = sn[kb];
+      ts[kb] = tsn[kb];
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+  };
+
   int j = 0;
-  f32x16 s[2], ts[2];
-  float mt = 0.0f;
-  // The hot loop only feeds the accumulators to MFMAs.  A tile whose row max
-  // moves the exponent base (always the first, rarely a later one) leaves the
-  // loop, rescales the accumulators outside it and re-enters.
+  // The hot loop only feeds the accumulators to MFMAs: a tile that moves the
+  // exponent base (rare after the first) leaves it, and the accumulators are
+  // rescaled outside before it re-enters.
   while (true) {
     bool rescale = false;
-    for (; j < nt; ++j) {
-      // the tile j copy must have landed for every wave before it is read
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      __syncthreads();
-      const char* cur = smem + (j & 1) * C::kStage;
-      if (j + 1 < nt) issue_tile(j + 1);
-
-      // ---- logits and tangent logits ------------------------------------
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        ts[kb] = f32x16{};
-      }
-#pragma unroll
-      for (int c = 0; c < C::kChunksD; ++c) {
-        const uint32_t u = krow + (((2 * c + hh) ^ ksw) << 4);
-        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(cur + u);
-        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(cur + 32 * C::kRow + u);
-        const bf16x8 tk0 = *reinterpret_cast<const bf16x8*>(cur + C::kTile + u);
-        const bf16x8 tk1 = *reinterpret_cast<const bf16x8*>(cur + C::kTile + 32 * C::kRow + u);
-        s[0] = mfma(k0, qf[c], s[0]);
-        s[1] = mfma(k1, qf[c], s[1]);
-        ts[0] = mfma(k0, tqf[c], ts[0]);
-        ts[1] = mfma(k1, tqf[c], ts[1]);
-        ts[0] = mfma(tk0, qf[c], ts[0]);
-        ts[1] = mfma(tk1, qf[c], ts[1]);
-      }
-
-      // ---- online softmax ------------------------------------------------
-      if (j == nt - 1 && (Lk % kBc) != 0) mask_tail<2>(s, Lk - j * kBc, hh);
-      mt = tile_max_log2<2>(s, c2);
+    while (j < nt - 2) {
+      iteration(j, false);
+      ++j;
       if (needs_rescale(st, mt)) {
         rescale = true;
         break;
       }
-      bf16x8 pf[4], ptf[4];
-      probabilities(s, ts, pf, ptf);
-      accumulate(cur, pf, ptf);
     }
     if (!rescale) break;
-    // ---- tile j with a new exponent base ----------------------------------
     const float alpha = apply_rescale(st, mt);
 #pragma unroll
     for (int b = 0; b < C::kBlocksD; ++b) {
       acc_o[b] *= alpha;
       acc_t[b] *= alpha;
     }
+  }
+  if (j == nt - 2) {  // the last tile's logits (masked if ragged)
+    iteration(j, ragged);
+    ++j;
+    if (needs_rescale(st, mt)) {
+      const float alpha = apply_rescale(st, mt);
+#pragma unroll
+      for (int b = 0; b < C::kBlocksD; ++b) {
+        acc_o[b] *= alpha;
+        acc_t[b] *= alpha;
+      }
+    }
+  }
+  {  // drain: the last tile's probabilities and products
     bf16x8 pf[4], ptf[4];
     probabilities(s, ts, pf, ptf);
-    accumulate(smem + (j & 1) * C::kStage, pf, ptf);
-    ++j;
+    accumulate(j, pf, ptf);
   }
 
   // ---- epilogue ------------------------------------------------------------

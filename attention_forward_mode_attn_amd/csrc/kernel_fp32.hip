@@ -41,12 +41,13 @@ struct Cfg {
   static_assert(kUnits % kThreads == 0, "tile split");
 };
 
-// K/tK rows are XOR-swizzled by 16-byte unit so that 32 lanes reading the same
-// column of 32 different rows hit distinct banks.  V/tV rows are not swizzled:
-// their readers take 32 consecutive floats of one row.
+// K/tK rows are XOR-swizzled by 16-byte unit so that the 16 lanes that a
+// 16-byte LDS read serves together (16 consecutive keys, same column) hit all
+// 16 bank groups of gfx950's 64-bank LDS.  V/tV rows are not swizzled: their
+// readers take 32 consecutive floats of one row.
 template <int D>
 __device__ inline uint32_t k_off(int r, int u) {
-  return r * (D * 4) + ((u ^ (r & 7)) << 4);
+  return r * (D * 4) + ((u ^ (r & 15)) << 4);
 }
 
 __device__ inline f32x16 mfma(float a, float b, f32x16 c) {
@@ -125,7 +126,7 @@ void attn_jvp_fp32_kernel(Params p) {
   RowState st = {-INFINITY, 0.0f, 0.0f};
   const float scale = p.scale;
   const float c2 = scale * kLog2e;
-  const int sw = n & 7;
+  const int sw = n & 15;
 
   // P and P*tS of one tile (fp32, straight from the S accumulator), and the
   // O / tO products: MFMA r pairs the keys that register r holds in the two halves.
@@ -176,7 +177,7 @@ void attn_jvp_fp32_kernel(Params p) {
       ts = f32x16{};
 #pragma unroll
       for (int i = 0; i < D / 8; ++i) {
-        // unit hh*D/8 + i of row n holds dims hh*D/2 + 4i .. +3
+        // logical unit hh*D/8 + i of row n holds dims hh*D/2 + 4i .. +3
         const uint32_t off = n * (D * 4) + (((hh * (D / 8) + i) ^ sw) << 4);
         const f32x4 kk = *reinterpret_cast<const f32x4*>(cur + off);
         const f32x4 tkk = *reinterpret_cast<const f32x4*>(cur + C::kTile + off);
