@@ -25,6 +25,8 @@
 //  * online softmax in the log2 domain with a lazily moved exponent base, per
 //    row running sums l = sum p and a = sum p*tS, and the epilogue
 //      O = acc_o / l,  tO = (acc_t - (a / l) acc_o) / l,  lse = (m + log2 l) ln 2.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -36,6 +38,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBc = 64;  // keys per tile
+#ifndef ATTNJVP_SPREAD_DMA
+#define ATTNJVP_SPREAD_DMA 1
+#endif
 
 struct Params {
   const void* q;
@@ -95,8 +100,17 @@ __device__ inline uint32_t tile_load_voff(int blk, int lane, bool vswz) {
   return (uint32_t)(r * C::kRow + u * 16);
 }
 
+// The copy is issued with inline asm rather than the builtin on purpose: the
+// compiler treats a builtin LDS DMA as a store that may alias every LDS read
+// that follows, and waits for it (vmcnt(0)) before the next read even though
+// the two stages never overlap.  Here the pipeline orders the copies itself:
+// each stage is refilled only after a barrier that follows its last read, and
+// read only after an explicit vmcnt(0) and a barrier.  The instruction has no
+// register outputs; its LDS destination (wave uniform) is passed in M0.
 __device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(dst) : "memory");
 }
 
 // LDS read helpers.
@@ -115,6 +129,37 @@ __device__ inline unsigned pack_bf16(float a, float b) {
 
 __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Scheduling fence: the compiler may not move instructions across it.  The
+// pipelined iteration is written as a sequence of small units (one MFMA plus a
+// slice of independent VALU work) separated by fences, so that the vector ALU
+// works while the matrix core runs instead of the two alternating in long runs.
+__device__ inline void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E).  Every
+// register-array index in the pipelined loop is a constant, so the arrays stay
+// in registers (a runtime index would send them to memory).
+template <int B, int E, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Logit MFMAs with the accumulator in VGPRs and the query operand in AGPRs.
+// The softmax reads the logits with VALU instructions, so they are produced
+// directly in VGPRs; the compiler would otherwise pick AGPR accumulators and
+// copy every logit out.  Ordering and hazards: these are only issued inside
+// the fenced units of the pipelined loop, where each accumulator chain uses
+// exactly-overlapping srcC (no wait states needed) and the first VALU read of
+// a result comes at least four MFMAs after it was written.
+__device__ inline void mfma_v0(f32x16& d, const bf16x8& a, const bf16x8& b) {  // d = a * b
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+}
+__device__ inline void mfma_v(f32x16& d, const bf16x8& a, const bf16x8& b) {  // d += a * b
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 
 template <int D>
@@ -158,6 +203,7 @@ void attn_jvp_bf16_kernel(Params p) {
   const float scale = p.scale;
   const float c2 = scale * kLog2e;
 
+  // ---- tile copies -----------------------------------------------------------
   // Per-lane global offsets of this wave's share of a tile copy (loop invariant).
   uint32_t voff_k[C::kLoadsPerWave], voff_v[C::kLoadsPerWave];
 #pragma unroll
@@ -168,26 +214,46 @@ void attn_jvp_bf16_kernel(Params p) {
   // LDS stage s holds K | tK | V | tV.  K/tK of tile j and V/tV of tile j live in
   // stage j & 1; the K half is fetched two tiles ahead, the V half one tile
   // ahead.  Tiles at or past the end are fetched as zeros (empty range).
-  auto issue = [&](int j, int tn0) {
+  // One 1 KB slice (i) of tensor tn's tile j.
+  auto issue_one = [&](int j, int tn, int i) {
     const int key0 = j * kBc;
     const uint32_t left = key0 < Lk ? (uint32_t)(Lk - key0) * D * 2 : 0u;
+    const auto r = make_rsrc(kbase[tn] + (size_t)key0 * D * 2, left);
     char* stage = smem + (j & 1) * C::kStage;
+    lds_dma16(r, stage + tn * C::kTile + (wv * C::kLoadsPerWave + i) * 1024, tn < 2 ? voff_k[i] : voff_v[i]);
+  };
+  auto issue = [&](int j, int tn0) {
 #pragma unroll
-    for (int tn = tn0; tn < tn0 + 2; ++tn) {
-      const auto r = make_rsrc(kbase[tn] + (size_t)key0 * D * 2, left);
+    for (int tn = tn0; tn < tn0 + 2; ++tn)
 #pragma unroll
-      for (int i = 0; i < C::kLoadsPerWave; ++i)
-        lds_dma16(r, stage + tn * C::kTile + (wv * C::kLoadsPerWave + i) * 1024, tn < 2 ? voff_k[i] : voff_v[i]);
-    }
+      for (int i = 0; i < C::kLoadsPerWave; ++i) issue_one(j, tn, i);
+  };
+  // The copies of one pipelined iteration (K|tK of tile j + 2, V|tV of tile
+  // j + 1), numbered q = 0 .. kDmaPerIter - 1.
+  constexpr int kDmaPerIter = 4 * C::kLoadsPerWave;
+  auto issue_q = [&](int j, auto iq) {
+    constexpr int q = decltype(iq)::value;
+    constexpr int tn = q / C::kLoadsPerWave, i = q % C::kLoadsPerWave;
+    issue_one(tn < 2 ? j + 2 : j + 1, tn, i);
   };
 
-  // Per-lane LDS read offsets.
+  // ---- fragment reads ------------------------------------------------------
   // K fragment (key block kb, dim chunk c): key 32kb + n, unit (2c + hh) ^ k_swz(n).
   const uint32_t krow = n * C::kRow;
   const int ksw = k_swz<D>(n);
+  auto load_k = [&](const char* stage, int c, bf16x8 (&kf)[4]) {
+    const uint32_t u = krow + (((2 * c + hh) ^ ksw) << 4);
+    kf[0] = *reinterpret_cast<const bf16x8*>(stage + u);
+    kf[1] = *reinterpret_cast<const bf16x8*>(stage + 32 * C::kRow + u);
+    kf[2] = *reinterpret_cast<const bf16x8*>(stage + C::kTile + u);
+    kf[3] = *reinterpret_cast<const bf16x8*>(stage + C::kTile + 32 * C::kRow + u);
+  };
   // V fragment via ds_read_b64_tr_b16: in 16-lane group G = lane / 16 (half
   // hh = G / 2, dims 16(G & 1) .. +15 of the 32-dim block), source lane s reads
-  // 4 dims starting at 4(s & 3) of key 4hh + (s >> 2) (+ 16cc + 8rho).
+  // 4 dims starting at 4(s & 3) of key 4hh + (s >> 2) (+ 16cc, + 8 for the
+  // second read).  The result has keys 16cc + 4hh + 0..3 in elements 0..3 and
+  // 16cc + 8 + 4hh + 0..3 in elements 4..7, which are exactly the keys the P
+  // operand registers of half hh hold.
   const int G = lane >> 4, sl = lane & 15;
   const int vkey = 4 * (G >> 1) + (sl >> 2);
   uint32_t voff_tr[C::kBlocksD];
@@ -196,153 +262,223 @@ void attn_jvp_bf16_kernel(Params p) {
     const int d0 = 32 * b + 16 * (G & 1) + 4 * (sl & 3);
     voff_tr[b] = vkey * C::kRow + ((((d0 >> 3) ^ v_swz<D>(vkey)) << 4) | ((d0 & 7) * 2));
   }
-
-  // S^T = K Q^T and tS^T = K tQ^T + tK Q^T of tile j (K half of stage j & 1).
-  auto logits = [&](int j, f32x16 (&s)[2], f32x16 (&ts)[2]) {
-    const char* cur = smem + (j & 1) * C::kStage;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      ts[kb] = f32x16{};
-    }
-#pragma unroll
-    for (int c = 0; c < C::kChunksD; ++c) {
-      const uint32_t u = krow + (((2 * c + hh) ^ ksw) << 4);
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(cur + u);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(cur + 32 * C::kRow + u);
-      const bf16x8 tk0 = *reinterpret_cast<const bf16x8*>(cur + C::kTile + u);
-      const bf16x8 tk1 = *reinterpret_cast<const bf16x8*>(cur + C::kTile + 32 * C::kRow + u);
-      s[0] = mfma(k0, qf[c], s[0]);
-      s[1] = mfma(k1, qf[c], s[1]);
-      ts[0] = mfma(k0, tqf[c], ts[0]);
-      ts[1] = mfma(k1, tqf[c], ts[1]);
-      ts[0] = mfma(tk0, qf[c], ts[0]);
-      ts[1] = mfma(tk1, qf[c], ts[1]);
-    }
+  // V^T (tn = 0) or tV^T (tn = 1) fragment of dim block b, key chunk cc
+  auto load_v = [&](const char* stage, int cc, int b, int tn) {
+    const char* vb = stage + (2 + tn) * C::kTile + 16 * cc * C::kRow + voff_tr[b];
+    const i16x4 lo = lds_tr16(vb), hi = lds_tr16(vb + 8 * C::kRow);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  // P and P*tS of one tile as bf16 B operands, accumulated into l and a:
-  // chunk cc (keys 16cc..16cc+15) is registers 8*(cc%2) .. +7 of key block cc/2.
-  auto probabilities = [&](const f32x16 (&s)[2], const f32x16 (&ts)[2], bf16x8 (&pf)[4], bf16x8 (&ptf)[4]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c2, -st.m));
-        const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c2, -st.m));
-        const float q0 = p0 * (ts[kb][r] * scale);
-        const float q1 = p1 * (ts[kb][r + 1] * scale);
-        st.l += p0 + p1;
-        st.a += q0 + q1;
-        const int cc = 2 * kb + (r >> 3), i = r & 7;
-        const unsigned pp = pack_bf16(p0, p1), qq = pack_bf16(q0, q1);
-        pf[cc][i] = __builtin_bit_cast(bf16x2, pp)[0];
-        pf[cc][i + 1] = __builtin_bit_cast(bf16x2, pp)[1];
-        ptf[cc][i] = __builtin_bit_cast(bf16x2, qq)[0];
-        ptf[cc][i + 1] = __builtin_bit_cast(bf16x2, qq)[1];
-      }
+  // ---- the six products and the softmax, as building blocks -----------------
+  // Logit element e (0..31) of a tile is register e % 16 of key block e / 16:
+  // key 32 (e / 16) + acc_row(e % 16, hh).
+  //
+  // S^T = K Q^T and tS^T = K tQ^T + tK Q^T of one 64-key tile, chunk c of the
+  // head dimension: 6 MFMAs (unit u = 0..5).
+  auto logit_mfma = [&](auto iu, auto ic, const bf16x8 (&k)[4], f32x16 (&sn)[2], f32x16 (&tsn)[2]) {
+    constexpr int u = decltype(iu)::value, c = decltype(ic)::value;
+    if constexpr (c == 0) {  // first chunk starts the accumulators
+      if constexpr (u == 0) mfma_v0(sn[0], k[0], qf[c]);
+      if constexpr (u == 1) mfma_v0(sn[1], k[1], qf[c]);
+      if constexpr (u == 2) mfma_v0(tsn[0], k[0], tqf[c]);
+      if constexpr (u == 3) mfma_v0(tsn[1], k[1], tqf[c]);
+    } else {
+      if constexpr (u == 0) mfma_v(sn[0], k[0], qf[c]);
+      if constexpr (u == 1) mfma_v(sn[1], k[1], qf[c]);
+      if constexpr (u == 2) mfma_v(tsn[0], k[0], tqf[c]);
+      if constexpr (u == 3) mfma_v(tsn[1], k[1], tqf[c]);
+    }
+    if constexpr (u == 4) mfma_v(tsn[0], k[2], qf[c]);
+    if constexpr (u == 5) mfma_v(tsn[1], k[3], qf[c]);
+  };
+  // Softmax element e: p = 2^(x - m), q = p * tS; l += p, a += q.  P and P*tS
+  // become bf16 B operands, packed on odd e: chunk cc (keys 16cc..16cc+15) is
+  // elements 8cc .. 8cc + 7.
+  struct Probs {
+    bf16x8 pf[4], ptf[4];
+  };
+  // pe, qe: p and p*tS of the last even element, waiting for their pair
+  auto element = [&](auto ie, const f32x16 (&sv)[2], const f32x16 (&tsv)[2], Probs& pr, float& pe, float& qe) {
+    constexpr int e = decltype(ie)::value;
+    const float pv = fast_exp2(__builtin_fmaf(sv[e >> 4][e & 15], c2, -st.m));
+    const float qv = pv * (tsv[e >> 4][e & 15] * scale);
+    st.l += pv;
+    st.a += qv;
+    if constexpr (e & 1) {
+      constexpr int cc = e >> 3, i = (e & 7) - 1;
+      const unsigned pp = pack_bf16(pe, pv), qq = pack_bf16(qe, qv);
+      pr.pf[cc][i] = __builtin_bit_cast(bf16x2, pp)[0];
+      pr.pf[cc][i + 1] = __builtin_bit_cast(bf16x2, pp)[1];
+      pr.ptf[cc][i] = __builtin_bit_cast(bf16x2, qq)[0];
+      pr.ptf[cc][i + 1] = __builtin_bit_cast(bf16x2, qq)[1];
+    } else {
+      pe = pv;
+      qe = qv;
     }
   };
-  // O^T += V^T P^T and tO^T += tV^T P^T + V^T (P*tS)^T for tile j.  The V^T
-  // fragment (dim block b, key chunk cc) has keys 16cc + 4hh + 0..3 in elements
-  // 0..3 and 16cc + 8 + 4hh + 0..3 in elements 4..7, matching the P registers.
-  auto accumulate = [&](int j, const bf16x8 (&pf)[4], const bf16x8 (&ptf)[4]) {
-    const char* cur = smem + (j & 1) * C::kStage;
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      bf16x8 vv[C::kBlocksD];
-#pragma unroll
-      for (int b = 0; b < C::kBlocksD; ++b) {
-        const char* vb = cur + 2 * C::kTile + 16 * cc * C::kRow + voff_tr[b];
-        const i16x4 lo = lds_tr16(vb), hi = lds_tr16(vb + 8 * C::kRow);
-        const char* tb = vb + C::kTile;
-        const i16x4 tlo = lds_tr16(tb), thi = lds_tr16(tb + 8 * C::kRow);
-        vv[b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        const bf16x8 tvv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(tlo, thi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc_o[b] = mfma(vv[b], pf[cc], acc_o[b]);
-        acc_t[b] = mfma(tvv, pf[cc], acc_t[b]);
-      }
-#pragma unroll
-      for (int b = 0; b < C::kBlocksD; ++b) acc_t[b] = mfma(vv[b], ptf[cc], acc_t[b]);
-    }
+  // O^T += V^T P^T and tO^T += tV^T P^T + V^T (P*tS)^T over one tile: 12 MFMAs
+  // per key chunk.  `work(unit)` runs after each MFMA; fragments are reloaded
+  // for the next chunk right after their last use.
+  auto products = [&](const char* stage, const Probs& pr, auto&& work) {
+    bf16x8 vf[C::kBlocksD], tvf[C::kBlocksD];
+    static_for<0, C::kBlocksD>([&](auto ib) {
+      constexpr int b = decltype(ib)::value;
+      vf[b] = load_v(stage, 0, b, 0);
+      tvf[b] = load_v(stage, 0, b, 1);
+    });
+    fence();
+    static_for<0, 4>([&](auto icc) {
+      constexpr int cc = decltype(icc)::value;
+      static_for<0, C::kBlocksD>([&](auto ib) {
+        constexpr int b = decltype(ib)::value;
+        acc_o[b] = mfma(vf[b], pr.pf[cc], acc_o[b]);
+        work(std::integral_constant<int, 3 * C::kBlocksD * cc + 2 * b>{});
+        fence();
+        acc_t[b] = mfma(tvf[b], pr.pf[cc], acc_t[b]);
+        if constexpr (cc + 1 < 4) tvf[b] = load_v(stage, cc + 1, b, 1);
+        work(std::integral_constant<int, 3 * C::kBlocksD * cc + 2 * b + 1>{});
+        fence();
+      });
+      static_for<0, C::kBlocksD>([&](auto ib) {
+        constexpr int b = decltype(ib)::value;
+        acc_t[b] = mfma(vf[b], pr.ptf[cc], acc_t[b]);
+        if constexpr (cc + 1 < 4) vf[b] = load_v(stage, cc + 1, b, 0);
+        work(std::integral_constant<int, 3 * C::kBlocksD * cc + 2 * C::kBlocksD + b>{});
+        fence();
+      });
+    });
   };
+  constexpr int kUnitsB = 12 * C::kBlocksD;  // MFMAs of products(), numbered 0 .. kUnitsB - 1
 
   const int nt = (Lk + kBc - 1) / kBc;
   const bool ragged = (Lk % kBc) != 0;
-  f32x16 s[2], ts[2];    // logits of the tile whose probabilities come next
-  f32x16 sn[2], tsn[2];  // logits of the following tile, being accumulated
+  f32x16 sv[2], tsv[2];  // logits of the tile whose probabilities come next
+  f32x16 nv[2], tnv[2];  // logits of the following tile
+  float mt;              // its row max (log2 domain)
 
-  // Prologue: tile 0 logits; its max sets the exponent base.
+  // ---- prologue: tile 0 logits; its max sets the exponent base --------------
   issue(0, 0);
   issue(0, 2);
   issue(1, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): all DMA of this wave landed
   __syncthreads();
-  logits(0, s, ts);
-  if (nt == 1 && ragged) mask_tail<2>(s, Lk, hh);
-  float mt = tile_max_log2<2>(s, c2);
-  apply_rescale(st, mt);  // accumulators are still zero
-  __syncthreads();        // every wave is done with K of tile 0 before it is refilled
+  {
+    static_for<0, C::kChunksD>([&](auto ic) {
+      bf16x8 k[4];
+      load_k(smem, decltype(ic)::value, k);
+      static_for<0, 6>([&](auto iu) { logit_mfma(iu, ic, k, sv, tsv); });
+    });
+    fence();
+    if (nt == 1 && ragged) mask_tail<2>(sv, Lk, hh);
+    mt = tile_max_log2<2>(sv, c2);
+    apply_rescale(st, mt);  // accumulators are still zero
+  }
+  __syncthreads();  // every wave is done with K of tile 0 before it is refilled
 
-  // Iteration j: probabilities of tile j while the logits of tile j + 1 are
-  // computed, then the O / tO products of tile j while the max of tile j + 1 is
-  // reduced.  In flight meanwhile: K of tile j + 2 and V of tile j + 1.
-  auto iteration = [&](int j, bool mask_next) {
+  // ---- one pipelined iteration ------------------------------------------------
+  // Phase A: the 48 logit MFMAs of tile j + 1, each paired with softmax
+  // elements of tile j.  Phase B: the 48 product MFMAs of tile j, each paired
+  // with moving logits of tile j + 1 out of the accumulators and into the row
+  // max.  In flight meanwhile: K of tile j + 2 and V of tile j + 1.
+  auto iteration = [&](int j, const f32x16 (&sv)[2], const f32x16 (&tsv)[2], f32x16 (&sn)[2], f32x16 (&tsn)[2],
+                       bool mask_next) {
+#if !ATTNJVP_SPREAD_DMA
     issue(j + 2, 0);
     issue(j + 1, 2);
-    bf16x8 pf[4], ptf[4];
-    probabilities(s, ts, pf, ptf);
-    logits(j + 1, sn, tsn);
-    accumulate(j, pf, ptf);
+#endif
+    const char* kstage = smem + ((j + 1) & 1) * C::kStage;
+    const char* vstage = smem + (j & 1) * C::kStage;
+
+    Probs pr;
+    float pe = 0.0f, qe = 0.0f;
+    bf16x8 kf[2][4];
+    load_k(kstage, 0, kf[0]);
+    fence();
+    constexpr int kEpc = 32 / C::kChunksD;  // softmax elements per chunk of 6 MFMAs
+    static_for<0, C::kChunksD>([&](auto ic) {
+      constexpr int c = decltype(ic)::value;
+      if constexpr (c + 1 < C::kChunksD) load_k(kstage, c + 1, kf[(c + 1) & 1]);
+      static_for<0, 6>([&](auto iu) {
+        constexpr int u = decltype(iu)::value;
+        logit_mfma(iu, ic, kf[c & 1], sn, tsn);
+        static_for<kEpc * c + (u * kEpc) / 6, kEpc * c + ((u + 1) * kEpc) / 6>(
+            [&](auto ie) { element(ie, sv, tsv, pr, pe, qe); });
+#if ATTNJVP_SPREAD_DMA
+        // the tile copies are spread over the phase-A units, one per
+        // (units / copies), instead of one burst at the top of the iteration
+        constexpr int g = 6 * c + u, kUnitsA = 6 * C::kChunksD;
+        static_for<(g * kDmaPerIter + kUnitsA - 1) / kUnitsA, ((g + 1) * kDmaPerIter + kUnitsA - 1) / kUnitsA>(
+            [&](auto iq) { issue_q(j, iq); });
+#endif
+        fence();
+      });
+    });
+
     if (mask_next) mask_tail<2>(sn, Lk - (j + 1) * kBc, hh);
-    mt = tile_max_log2<2>(sn, c2);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = sn[kb];
-      ts[kb] = tsn[kb];
-    }
+    float mx = -INFINITY;
+    products(vstage, pr, [&](auto iunit) {
+      constexpr int unit = decltype(iunit)::value;
+      static_for<(unit * 32) / kUnitsB, ((unit + 1) * 32) / kUnitsB>([&](auto ix) {
+        constexpr int x = decltype(ix)::value;
+        mx = fmaxf(mx, sn[x >> 4][x & 15]);
+      });
+    });
+    mt = xhalf_max(mx) * c2;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
   };
 
-  int j = 0;
-  // The hot loop only feeds the accumulators to MFMAs: a tile that moves the
-  // exponent base (rare after the first) leaves it, and the accumulators are
-  // rescaled outside before it re-enters.
-  while (true) {
-    bool rescale = false;
-    while (j < nt - 2) {
-      iteration(j, false);
-      ++j;
-      if (needs_rescale(st, mt)) {
-        rescale = true;
-        break;
-      }
-    }
-    if (!rescale) break;
-    const float alpha = apply_rescale(st, mt);
+  auto rescale_acc = [&](float alpha) {
 #pragma unroll
     for (int b = 0; b < C::kBlocksD; ++b) {
       acc_o[b] *= alpha;
       acc_t[b] *= alpha;
     }
+  };
+  auto take_next = [&]() {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sv[kb] = nv[kb];
+      tsv[kb] = tnv[kb];
+    }
+  };
+
+  // ---- main loop --------------------------------------------------------------
+  // The hot loop only feeds the accumulators to MFMAs: a tile that moves the
+  // exponent base (rare after the first) leaves it, and the accumulators are
+  // rescaled outside before it re-enters.  It is unrolled twice so that the
+  // logits alternate between (sv, tsv) and (nv, tnv) without copies; at the
+  // top of the outer loop the logits of tile j are in (sv, tsv).
+  int j = 0;
+  while (true) {
+    bool rescale = false;
+    while (j < nt - 2) {
+      iteration(j, sv, tsv, nv, tnv, false);
+      ++j;
+      rescale = needs_rescale(st, mt);
+      if (rescale || j >= nt - 2) {
+        take_next();
+        break;
+      }
+      iteration(j, nv, tnv, sv, tsv, false);
+      ++j;
+      rescale = needs_rescale(st, mt);
+      if (rescale) break;
+    }
+    if (!rescale) break;
+    rescale_acc(apply_rescale(st, mt));
   }
   if (j == nt - 2) {  // the last tile's logits (masked if ragged)
-    iteration(j, ragged);
+    iteration(j, sv, tsv, nv, tnv, ragged);
     ++j;
-    if (needs_rescale(st, mt)) {
-      const float alpha = apply_rescale(st, mt);
-#pragma unroll
-      for (int b = 0; b < C::kBlocksD; ++b) {
-        acc_o[b] *= alpha;
-        acc_t[b] *= alpha;
-      }
-    }
+    take_next();
+    if (needs_rescale(st, mt)) rescale_acc(apply_rescale(st, mt));
   }
   {  // drain: the last tile's probabilities and products
-    bf16x8 pf[4], ptf[4];
-    probabilities(s, ts, pf, ptf);
-    accumulate(j, pf, ptf);
+    Probs pr;
+    float pe = 0.0f, qe = 0.0f;
+    static_for<0, 32>([&](auto ie) { element(ie, sv, tsv, pr, pe, qe); });
+    products(smem + (j & 1) * C::kStage, pr, [](auto) {});
   }
 
   // ---- epilogue ------------------------------------------------------------
