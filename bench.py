@@ -55,8 +55,12 @@ def measured_traffic(workload: str):
     return float(m_b.group(1))
 
 
-def cpu_baseline(w, budget_s: float = 20.0):
-    """Time the fp64 oracle on sampled query rows of the same workload."""
+def cpu_baseline(w, budget_s: float = 30.0, rows_per_head: int = 1024):
+    """Time the fp64 oracle on sampled query rows of the same workload.
+
+    Every head contributes ``rows_per_head`` query rows (both tile edges, the
+    ragged tail and seeded random rows) against all of its keys; heads are
+    added until the time budget is spent."""
     import numpy as np
 
     from oracle import attention_jvp_head
@@ -74,7 +78,7 @@ def cpu_baseline(w, budget_s: float = 20.0):
     for b in range(w.B):
         for h in range(w.H):
             a = {t: head_array(w, t, b, h) for t in TENSORS}
-            rows = sample_rows(w, b, h)
+            rows = sample_rows(w, b, h, n_random=max(0, rows_per_head - 32))
             t0 = time.perf_counter()
             attention_jvp_head(a["q"], a["k"], a["v"], a["tq"], a["tk"], a["tv"], w.scale, rows=rows)
             t_total += time.perf_counter() - t0
@@ -105,7 +109,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="video_self_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-budget", type=float, default=30.0)
+    ap.add_argument("--cpu-rows-per-head", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -207,7 +212,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 oracle on sampled rows (cpu_baseline)", file=sys.stderr, flush=True)
-        cb = cpu_baseline(w, args.cpu_budget)
+        cb = cpu_baseline(w, args.cpu_budget, args.cpu_rows_per_head)
         cb.pop("_np", None)
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
