@@ -24,7 +24,11 @@
 //    accumulator layout of P, so V never needs an explicit transpose;
 //  * online softmax in the log2 domain with a lazily moved exponent base, per
 //    row running sums l = sum p and a = sum p*tS, and the epilogue
-//      O = acc_o / l,  tO = (acc_t - (a / l) acc_o) / l,  lse = (m + log2 l) ln 2.
+//      O = acc_o / l,  tO = (acc_t - (a / l) acc_o) / l,  lse = (m + log2 l) ln 2;
+//  * software pipeline: iteration j computes the softmax of tile j under the
+//    logit MFMAs of tile j + 1 (phase A), then the product MFMAs of tile j under
+//    the max reduction of tile j + 1 (phase B), written as fenced units of one
+//    MFMA plus a slice of VALU work so that the two execute together.
 #include <type_traits>
 
 #include "device_common.h"
@@ -38,9 +42,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBc = 64;  // keys per tile
-#ifndef ATTNJVP_SPREAD_DMA
-#define ATTNJVP_SPREAD_DMA 1
-#endif
 
 struct Params {
   const void* q;
@@ -146,20 +147,6 @@ __device__ inline void static_for(F&& f) {
     f(std::integral_constant<int, B>{});
     static_for<B + 1, E>(f);
   }
-}
-
-// Logit MFMAs with the accumulator in VGPRs and the query operand in AGPRs.
-// The softmax reads the logits with VALU instructions, so they are produced
-// directly in VGPRs; the compiler would otherwise pick AGPR accumulators and
-// copy every logit out.  Ordering and hazards: these are only issued inside
-// the fenced units of the pipelined loop, where each accumulator chain uses
-// exactly-overlapping srcC (no wait states needed) and the first VALU read of
-// a result comes at least four MFMAs after it was written.
-__device__ inline void mfma_v0(f32x16& d, const bf16x8& a, const bf16x8& b) {  // d = a * b
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
-}
-__device__ inline void mfma_v(f32x16& d, const bf16x8& a, const bf16x8& b) {  // d += a * b
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
 }
 
 template <int D>
@@ -277,19 +264,12 @@ void attn_jvp_bf16_kernel(Params p) {
   // head dimension: 6 MFMAs (unit u = 0..5).
   auto logit_mfma = [&](auto iu, auto ic, const bf16x8 (&k)[4], f32x16 (&sn)[2], f32x16 (&tsn)[2]) {
     constexpr int u = decltype(iu)::value, c = decltype(ic)::value;
-    if constexpr (c == 0) {  // first chunk starts the accumulators
-      if constexpr (u == 0) mfma_v0(sn[0], k[0], qf[c]);
-      if constexpr (u == 1) mfma_v0(sn[1], k[1], qf[c]);
-      if constexpr (u == 2) mfma_v0(tsn[0], k[0], tqf[c]);
-      if constexpr (u == 3) mfma_v0(tsn[1], k[1], tqf[c]);
-    } else {
-      if constexpr (u == 0) mfma_v(sn[0], k[0], qf[c]);
-      if constexpr (u == 1) mfma_v(sn[1], k[1], qf[c]);
-      if constexpr (u == 2) mfma_v(tsn[0], k[0], tqf[c]);
-      if constexpr (u == 3) mfma_v(tsn[1], k[1], tqf[c]);
-    }
-    if constexpr (u == 4) mfma_v(tsn[0], k[2], qf[c]);
-    if constexpr (u == 5) mfma_v(tsn[1], k[3], qf[c]);
+    if constexpr (u == 0) sn[0] = mfma(k[0], qf[c], c == 0 ? f32x16{} : sn[0]);
+    if constexpr (u == 1) sn[1] = mfma(k[1], qf[c], c == 0 ? f32x16{} : sn[1]);
+    if constexpr (u == 2) tsn[0] = mfma(k[0], tqf[c], c == 0 ? f32x16{} : tsn[0]);
+    if constexpr (u == 3) tsn[1] = mfma(k[1], tqf[c], c == 0 ? f32x16{} : tsn[1]);
+    if constexpr (u == 4) tsn[0] = mfma(k[2], qf[c], tsn[0]);
+    if constexpr (u == 5) tsn[1] = mfma(k[3], qf[c], tsn[1]);
   };
   // Softmax element e: p = 2^(x - m), q = p * tS; l += p, a += q.  P and P*tS
   // become bf16 B operands, packed on odd e: chunk cc (keys 16cc..16cc+15) is
@@ -382,10 +362,6 @@ void attn_jvp_bf16_kernel(Params p) {
   // max.  In flight meanwhile: K of tile j + 2 and V of tile j + 1.
   auto iteration = [&](int j, const f32x16 (&sv)[2], const f32x16 (&tsv)[2], f32x16 (&sn)[2], f32x16 (&tsn)[2],
                        bool mask_next) {
-#if !ATTNJVP_SPREAD_DMA
-    issue(j + 2, 0);
-    issue(j + 1, 2);
-#endif
     const char* kstage = smem + ((j + 1) & 1) * C::kStage;
     const char* vstage = smem + (j & 1) * C::kStage;
 
@@ -403,13 +379,12 @@ void attn_jvp_bf16_kernel(Params p) {
         logit_mfma(iu, ic, kf[c & 1], sn, tsn);
         static_for<kEpc * c + (u * kEpc) / 6, kEpc * c + ((u + 1) * kEpc) / 6>(
             [&](auto ie) { element(ie, sv, tsv, pr, pe, qe); });
-#if ATTNJVP_SPREAD_DMA
-        // the tile copies are spread over the phase-A units, one per
-        // (units / copies), instead of one burst at the top of the iteration
+        // the tile copies of this iteration (K|tK of tile j + 2, V|tV of tile
+        // j + 1) are spread over the phase-A units instead of one burst at the
+        // top, where they would compete with the first K fragment reads
         constexpr int g = 6 * c + u, kUnitsA = 6 * C::kChunksD;
         static_for<(g * kDmaPerIter + kUnitsA - 1) / kUnitsA, ((g + 1) * kDmaPerIter + kUnitsA - 1) / kUnitsA>(
             [&](auto iq) { issue_q(j, iq); });
-#endif
         fence();
       });
     });
