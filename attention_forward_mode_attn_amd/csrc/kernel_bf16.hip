@@ -107,11 +107,15 @@ __device__ inline uint32_t tile_load_voff(int blk, int lane, bool vswz) {
 // the two stages never overlap.  Here the pipeline orders the copies itself:
 // each stage is refilled only after a barrier that follows its last read, and
 // read only after an explicit vmcnt(0) and a barrier.  The instruction has no
-// register outputs; its LDS destination (wave uniform) is passed in M0.
-__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
-  const uint32_t dst = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(dst) : "memory");
+// register outputs; its LDS destination (a wave-uniform LDS byte address) is
+// passed in M0.
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(lds_addr) : "memory");
+}
+
+// LDS byte address of a __shared__ object.
+__device__ inline uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
 
 // LDS read helpers.
@@ -128,6 +132,12 @@ __device__ inline unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
 }
 
+// c + x.lo + x.hi for a packed bf16 pair x (fp32 arithmetic).
+__device__ inline float sum_bf16x2(unsigned x, float c) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, c, false);
+}
+
 __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -138,9 +148,18 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 // works while the matrix core runs instead of the two alternating in long runs.
 __device__ inline void fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// Keep a value computed here.  Values that are only used in the next
+// iteration (the running sums, the logits waiting for their softmax) would
+// otherwise be sunk by the optimizer past the fences to the loop latch, where
+// they run as one long VALU block with the matrix core idle.
+__device__ inline void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ inline void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
+
 // Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E).  Every
 // register-array index in the pipelined loop is a constant, so the arrays stay
 // in registers (a runtime index would send them to memory).
+template <int I>
+using IC = std::integral_constant<int, I>;
 template <int B, int E, typename F>
 __device__ inline void static_for(F&& f) {
   if constexpr (B < E) {
@@ -166,8 +185,12 @@ void attn_jvp_bf16_kernel(Params p) {
   const uint32_t qbytes = (uint32_t)Lq * D * 2;
   const auto rq = make_rsrc((const char*)p.q + qhead, qbytes);
   const auto rtq = make_rsrc((const char*)p.tq + qhead, qbytes);
-  const char* kbase[4] = {(const char*)p.k + khead, (const char*)p.tk + khead,
-                          (const char*)p.v + khead, (const char*)p.tv + khead};
+  // One resource per tensor over this head's Lk rows: tiles are addressed by
+  // the per-lane offset, and rows at or past Lk read as zero.
+  const uint32_t kbytes = (uint32_t)Lk * D * 2;
+  const __amdgpu_buffer_rsrc_t rkv[4] = {
+      make_rsrc((const char*)p.k + khead, kbytes), make_rsrc((const char*)p.tk + khead, kbytes),
+      make_rsrc((const char*)p.v + khead, kbytes), make_rsrc((const char*)p.tv + khead, kbytes)};
 
   // Q and tQ fragments (B operand of S^T = K Q^T): lane (n, hh) holds dims
   // 16c + 8hh .. +7 of its query row.  Rows past Lq read as zero.
@@ -200,14 +223,13 @@ void attn_jvp_bf16_kernel(Params p) {
   }
   // LDS stage s holds K | tK | V | tV.  K/tK of tile j and V/tV of tile j live in
   // stage j & 1; the K half is fetched two tiles ahead, the V half one tile
-  // ahead.  Tiles at or past the end are fetched as zeros (empty range).
+  // ahead.  Tiles at or past the end are fetched as zeros (out of range).
   // One 1 KB slice (i) of tensor tn's tile j.
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_address(smem));
   auto issue_one = [&](int j, int tn, int i) {
-    const int key0 = j * kBc;
-    const uint32_t left = key0 < Lk ? (uint32_t)(Lk - key0) * D * 2 : 0u;
-    const auto r = make_rsrc(kbase[tn] + (size_t)key0 * D * 2, left);
-    char* stage = smem + (j & 1) * C::kStage;
-    lds_dma16(r, stage + tn * C::kTile + (wv * C::kLoadsPerWave + i) * 1024, tn < 2 ? voff_k[i] : voff_v[i]);
+    const uint32_t toff = (uint32_t)j * C::kTile;
+    const uint32_t dst = smem_lds + (j & 1) * C::kStage + tn * C::kTile + (wv * C::kLoadsPerWave + i) * 1024;
+    lds_dma16(rkv[tn], dst, (tn < 2 ? voff_k[i] : voff_v[i]) + toff);
   };
   auto issue = [&](int j, int tn0) {
 #pragma unroll
@@ -271,42 +293,107 @@ void attn_jvp_bf16_kernel(Params p) {
     if constexpr (u == 4) tsn[0] = mfma(k[2], qf[c], tsn[0]);
     if constexpr (u == 5) tsn[1] = mfma(k[3], qf[c], tsn[1]);
   };
-  // Softmax element e: p = 2^(x - m), q = p * tS; l += p, a += q.  P and P*tS
-  // become bf16 B operands, packed on odd e: chunk cc (keys 16cc..16cc+15) is
-  // elements 8cc .. 8cc + 7.
-  struct Probs {
-    bf16x8 pf[4], ptf[4];
+  // The logits of a tile wait for their softmax in VGPRs, already in the form
+  // the exponentials need: y = S * scale * log2(e) - m (so p = 2^y) and
+  // ts = tS * scale.  Element e (0..31) is register e % 16 of key block e / 16.
+  float yv[32], tsv[32];
+  // Moving the 64 logits of the tile just computed (accumulators sn, tsn; S
+  // then tS, x = 0..63) into (yv, tsv) takes three steps per value: read it
+  // out of the accumulator, transform it, fold y into the row max.
+  struct Take {
+    float raw[64];
+    float mx;
   };
-  // pe, qe: p and p*tS of the last even element, waiting for their pair
-  auto element = [&](auto ie, const f32x16 (&sv)[2], const f32x16 (&tsv)[2], Probs& pr, float& pe, float& qe) {
-    constexpr int e = decltype(ie)::value;
-    const float pv = fast_exp2(__builtin_fmaf(sv[e >> 4][e & 15], c2, -st.m));
-    const float qv = pv * (tsv[e >> 4][e & 15] * scale);
-    st.l += pv;
-    st.a += qv;
-    if constexpr (e & 1) {
-      constexpr int cc = e >> 3, i = (e & 7) - 1;
-      const unsigned pp = pack_bf16(pe, pv), qq = pack_bf16(qe, qv);
-      pr.pf[cc][i] = __builtin_bit_cast(bf16x2, pp)[0];
-      pr.pf[cc][i + 1] = __builtin_bit_cast(bf16x2, pp)[1];
-      pr.ptf[cc][i] = __builtin_bit_cast(bf16x2, qq)[0];
-      pr.ptf[cc][i + 1] = __builtin_bit_cast(bf16x2, qq)[1];
-    } else {
-      pe = pv;
-      qe = qv;
+  auto take_step = [&](auto is, auto ix, Take& tk, const f32x16 (&sn)[2], const f32x16 (&tsn)[2]) {
+    constexpr int step = decltype(is)::value, x = decltype(ix)::value;
+    if constexpr (step == 0) {
+      tk.raw[x] = x < 32 ? sn[x >> 4][x & 15] : tsn[(x - 32) >> 4][x & 15];
+      pin(tk.raw[x]);
+    } else if constexpr (step == 1) {
+      if constexpr (x < 32) {
+        yv[x] = __builtin_fmaf(tk.raw[x], c2, -st.m);
+        pin(yv[x]);
+      } else {
+        tsv[x - 32] = tk.raw[x] * scale;
+        pin(tsv[x - 32]);
+      }
+    } else if constexpr (x < 32) {
+      tk.mx = fmaxf(tk.mx, yv[x]);
     }
   };
-  // O^T += V^T P^T and tO^T += tV^T P^T + V^T (P*tS)^T over one tile: 12 MFMAs
-  // per key chunk.  `work(unit)` runs after each MFMA; fragments are reloaded
-  // for the next chunk right after their last use.
-  auto products = [&](const char* stage, const Probs& pr, auto&& work) {
-    bf16x8 vf[C::kBlocksD], tvf[C::kBlocksD];
+  // Softmax element e: p = 2^y, q = p * ts.  P and P*tS become bf16 B
+  // operands, packed in pairs: chunk cc (keys 16cc..16cc+15) is elements
+  // 8cc .. 8cc + 7.  l += p is summed in fp32 (it sets O's normaliser and the
+  // log-sum-exp); a += q is taken over the packed bf16 pairs (one dot2 with
+  // (1, 1) per pair), the same rounded values that the tO products consume.
+  // Four steps per element: exp; q and l; pack (odd e); a and the operands.
+  struct Probs {
+    bf16x8 pf[4], ptf[4];
+    float p[32], q[32];
+    unsigned pp[16], qq[16];
+  };
+  auto elem_step = [&](auto is, auto ie, Probs& pr) {
+    constexpr int step = decltype(is)::value, e = decltype(ie)::value;
+    if constexpr (step == 0) {
+      pr.p[e] = fast_exp2(yv[e]);
+      pin(pr.p[e]);
+    } else if constexpr (step == 1) {
+      pr.q[e] = pr.p[e] * tsv[e];
+      pin(pr.q[e]);
+      st.l += pr.p[e];
+      pin(st.l);
+    } else if constexpr (step == 2) {
+      if constexpr (e & 1) {
+        pr.pp[e >> 1] = pack_bf16(pr.p[e - 1], pr.p[e]);
+        pr.qq[e >> 1] = pack_bf16(pr.q[e - 1], pr.q[e]);
+        pin(pr.pp[e >> 1]);
+        pin(pr.qq[e >> 1]);
+      }
+    } else if constexpr (e & 1) {
+      constexpr int cc = e >> 3, i = (e & 7) - 1;
+      st.a = sum_bf16x2(pr.qq[e >> 1], st.a);
+      pin(st.a);
+      pr.pf[cc][i] = __builtin_bit_cast(bf16x2, pr.pp[e >> 1])[0];
+      pr.pf[cc][i + 1] = __builtin_bit_cast(bf16x2, pr.pp[e >> 1])[1];
+      pr.ptf[cc][i] = __builtin_bit_cast(bf16x2, pr.qq[e >> 1])[0];
+      pr.ptf[cc][i + 1] = __builtin_bit_cast(bf16x2, pr.qq[e >> 1])[1];
+    }
+  };
+  // Software pipeline over a sequence of N units that handle n items (N
+  // units, items [g n / N, (g + 1) n / N) start in unit g): unit g runs step s
+  // of the items that started in unit g - s, so that no instruction of a unit
+  // waits for another of the same unit (one wave issues in order; a dependent
+  // VALU op would hold back the next MFMA).  Slot g runs for g in [0, N + S - 1).
+  auto pipeline_slot = [&](auto ig, auto in_units, auto in_items, auto in_steps, auto&& step) {
+    constexpr int g = decltype(ig)::value, N = decltype(in_units)::value;
+    constexpr int n = decltype(in_items)::value, S = decltype(in_steps)::value;
+    static_for<0, S>([&](auto is) {
+      constexpr int s = S - 1 - decltype(is)::value;  // oldest items first
+      constexpr int u = g - s;
+      if constexpr (u >= 0 && u < N)
+        static_for<(u * n) / N, ((u + 1) * n) / N>([&](auto ix) { step(std::integral_constant<int, s>{}, ix); });
+    });
+  };
+  // All steps of items [X0, X1) at once (prologue and drain, no MFMA to hide under).
+  auto all_steps = [&](auto ix0, auto ix1, auto in_steps, auto&& step) {
+    static_for<decltype(ix0)::value, decltype(ix1)::value>([&](auto ix) {
+      static_for<0, decltype(in_steps)::value>([&](auto is) { step(is, ix); });
+    });
+  };
+  // V and tV fragments of key chunk 0, read ahead of the products.
+  auto load_v0 = [&](const char* stage, bf16x8 (&vf)[C::kBlocksD], bf16x8 (&tvf)[C::kBlocksD]) {
     static_for<0, C::kBlocksD>([&](auto ib) {
       constexpr int b = decltype(ib)::value;
       vf[b] = load_v(stage, 0, b, 0);
       tvf[b] = load_v(stage, 0, b, 1);
     });
-    fence();
+  };
+  // O^T += V^T P^T and tO^T += tV^T P^T + V^T (P*tS)^T over one tile: 12 MFMAs
+  // per key chunk, starting from the chunk-0 fragments in (vf, tvf).
+  // `work(unit)` runs after each MFMA; fragments are reloaded for the next
+  // chunk right after their last use.
+  auto products = [&](const char* stage, const Probs& pr, bf16x8 (&vf)[C::kBlocksD], bf16x8 (&tvf)[C::kBlocksD],
+                      auto&& work) {
     static_for<0, 4>([&](auto icc) {
       constexpr int cc = decltype(icc)::value;
       static_for<0, C::kBlocksD>([&](auto ib) {
@@ -328,13 +415,13 @@ void attn_jvp_bf16_kernel(Params p) {
       });
     });
   };
+  constexpr int kUnitsA = 6 * C::kChunksD;   // logit MFMAs of one tile
+  constexpr int kPreSlots = 2;               // softmax slots run before the first logit MFMA
   constexpr int kUnitsB = 12 * C::kBlocksD;  // MFMAs of products(), numbered 0 .. kUnitsB - 1
 
   const int nt = (Lk + kBc - 1) / kBc;
   const bool ragged = (Lk % kBc) != 0;
-  f32x16 sv[2], tsv[2];  // logits of the tile whose probabilities come next
-  f32x16 nv[2], tnv[2];  // logits of the following tile
-  float mt;              // its row max (log2 domain)
+  float my;  // row max of y over the tile waiting in (yv, tsv)
 
   // ---- prologue: tile 0 logits; its max sets the exponent base --------------
   issue(0, 0);
@@ -343,46 +430,51 @@ void attn_jvp_bf16_kernel(Params p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): all DMA of this wave landed
   __syncthreads();
   {
+    f32x16 sn[2], tsn[2];
     static_for<0, C::kChunksD>([&](auto ic) {
       bf16x8 k[4];
       load_k(smem, decltype(ic)::value, k);
-      static_for<0, 6>([&](auto iu) { logit_mfma(iu, ic, k, sv, tsv); });
+      static_for<0, 6>([&](auto iu) { logit_mfma(iu, ic, k, sn, tsn); });
     });
     fence();
-    if (nt == 1 && ragged) mask_tail<2>(sv, Lk, hh);
-    mt = tile_max_log2<2>(sv, c2);
-    apply_rescale(st, mt);  // accumulators are still zero
+    if (nt == 1 && ragged) mask_tail<2>(sn, Lk, hh);
+    st.m = tile_max_log2<2>(sn, c2);
+    Take tk;
+    all_steps(IC<0>{}, IC<64>{}, IC<2>{}, [&](auto is, auto ix) { take_step(is, ix, tk, sn, tsn); });
   }
   __syncthreads();  // every wave is done with K of tile 0 before it is refilled
 
   // ---- one pipelined iteration ------------------------------------------------
   // Phase A: the 48 logit MFMAs of tile j + 1, each paired with softmax
   // elements of tile j.  Phase B: the 48 product MFMAs of tile j, each paired
-  // with moving logits of tile j + 1 out of the accumulators and into the row
-  // max.  In flight meanwhile: K of tile j + 2 and V of tile j + 1.
-  auto iteration = [&](int j, const f32x16 (&sv)[2], const f32x16 (&tsv)[2], f32x16 (&sn)[2], f32x16 (&tsn)[2],
-                       bool mask_next) {
+  // with moving logits of tile j + 1 out of the accumulators into (yv, tsv)
+  // and the row max.  In flight meanwhile: K of tile j + 2 and V of tile j + 1.
+  auto iteration = [&](int j, bool mask_next) {
     const char* kstage = smem + ((j + 1) & 1) * C::kStage;
     const char* vstage = smem + (j & 1) * C::kStage;
 
+    f32x16 sn[2], tsn[2];
     Probs pr;
-    float pe = 0.0f, qe = 0.0f;
+    auto elem = [&](auto is, auto ie) { elem_step(is, ie, pr); };
     bf16x8 kf[2][4];
+    bf16x8 vf[C::kBlocksD], tvf[C::kBlocksD];
     load_k(kstage, 0, kf[0]);
+    // while the first K fragments are in flight: the first softmax slots
+    static_for<0, kPreSlots>([&](auto ig) { pipeline_slot(ig, IC<kUnitsA>{}, IC<32>{}, IC<4>{}, elem); });
     fence();
-    constexpr int kEpc = 32 / C::kChunksD;  // softmax elements per chunk of 6 MFMAs
     static_for<0, C::kChunksD>([&](auto ic) {
       constexpr int c = decltype(ic)::value;
       if constexpr (c + 1 < C::kChunksD) load_k(kstage, c + 1, kf[(c + 1) & 1]);
+      // the chunk-0 V fragments of the products are read under the last chunk
+      if constexpr (c + 1 == C::kChunksD) load_v0(vstage, vf, tvf);
       static_for<0, 6>([&](auto iu) {
         constexpr int u = decltype(iu)::value;
         logit_mfma(iu, ic, kf[c & 1], sn, tsn);
-        static_for<kEpc * c + (u * kEpc) / 6, kEpc * c + ((u + 1) * kEpc) / 6>(
-            [&](auto ie) { element(ie, sv, tsv, pr, pe, qe); });
+        constexpr int g = 6 * c + u;
+        pipeline_slot(IC<g + kPreSlots>{}, IC<kUnitsA>{}, IC<32>{}, IC<4>{}, elem);
         // the tile copies of this iteration (K|tK of tile j + 2, V|tV of tile
         // j + 1) are spread over the phase-A units instead of one burst at the
         // top, where they would compete with the first K fragment reads
-        constexpr int g = 6 * c + u, kUnitsA = 6 * C::kChunksD;
         static_for<(g * kDmaPerIter + kUnitsA - 1) / kUnitsA, ((g + 1) * kDmaPerIter + kUnitsA - 1) / kUnitsA>(
             [&](auto iq) { issue_q(j, iq); });
         fence();
@@ -390,70 +482,73 @@ void attn_jvp_bf16_kernel(Params p) {
     });
 
     if (mask_next) mask_tail<2>(sn, Lk - (j + 1) * kBc, hh);
-    float mx = -INFINITY;
-    products(vstage, pr, [&](auto iunit) {
+    Take tk;
+    tk.mx = -INFINITY;
+    auto take = [&](auto is, auto ix) { take_step(is, ix, tk, sn, tsn); };
+    products(vstage, pr, vf, tvf, [&](auto iunit) {
       constexpr int unit = decltype(iunit)::value;
-      static_for<(unit * 32) / kUnitsB, ((unit + 1) * 32) / kUnitsB>([&](auto ix) {
-        constexpr int x = decltype(ix)::value;
-        mx = fmaxf(mx, sn[x >> 4][x & 15]);
-      });
+      // the last softmax steps of tile j run under its first product MFMAs
+      // (they complete chunk 3, which the products reach last)
+      if constexpr (unit + kPreSlots < 3)
+        pipeline_slot(IC<kUnitsA + kPreSlots + unit>{}, IC<kUnitsA>{}, IC<32>{}, IC<4>{}, elem);
+      pipeline_slot(iunit, IC<kUnitsB>{}, IC<64>{}, IC<3>{}, take);
     });
-    mt = xhalf_max(mx) * c2;
+    pipeline_slot(IC<kUnitsB>{}, IC<kUnitsB>{}, IC<64>{}, IC<3>{}, take);
+    pipeline_slot(IC<kUnitsB + 1>{}, IC<kUnitsB>{}, IC<64>{}, IC<3>{}, take);
+    my = xhalf_max(tk.mx);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
   };
 
-  auto rescale_acc = [&](float alpha) {
+  // A tile whose max exceeds the exponent base by more than kRescaleSlack moves
+  // the base of its rows up to that max: the sums and accumulators are scaled
+  // by 2^-delta and the waiting logits shifted by -delta.
+  auto rescale = [&]() {
+    const float delta = my > kRescaleSlack ? my : 0.0f;
+    const float alpha = fast_exp2(-delta);
+    st.m += delta;
+    st.l *= alpha;
+    st.a *= alpha;
+#pragma unroll
+    for (int x = 0; x < 32; ++x) yv[x] -= delta;
 #pragma unroll
     for (int b = 0; b < C::kBlocksD; ++b) {
       acc_o[b] *= alpha;
       acc_t[b] *= alpha;
     }
   };
-  auto take_next = [&]() {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sv[kb] = nv[kb];
-      tsv[kb] = tnv[kb];
-    }
-  };
+  auto needs_rescale = [&]() { return __builtin_amdgcn_ballot_w64(my > kRescaleSlack) != 0; };
 
   // ---- main loop --------------------------------------------------------------
   // The hot loop only feeds the accumulators to MFMAs: a tile that moves the
   // exponent base (rare after the first) leaves it, and the accumulators are
-  // rescaled outside before it re-enters.  It is unrolled twice so that the
-  // logits alternate between (sv, tsv) and (nv, tnv) without copies; at the
-  // top of the outer loop the logits of tile j are in (sv, tsv).
+  // rescaled outside before it re-enters.  The logits of the last tile (masked
+  // when ragged) are computed by a peeled iteration.
   int j = 0;
   while (true) {
-    bool rescale = false;
+    bool moved = false;
     while (j < nt - 2) {
-      iteration(j, sv, tsv, nv, tnv, false);
+      iteration(j, false);
       ++j;
-      rescale = needs_rescale(st, mt);
-      if (rescale || j >= nt - 2) {
-        take_next();
+      if (needs_rescale()) {
+        moved = true;
         break;
       }
-      iteration(j, nv, tnv, sv, tsv, false);
-      ++j;
-      rescale = needs_rescale(st, mt);
-      if (rescale) break;
     }
-    if (!rescale) break;
-    rescale_acc(apply_rescale(st, mt));
+    if (!moved) break;
+    rescale();
   }
-  if (j == nt - 2) {  // the last tile's logits (masked if ragged)
-    iteration(j, sv, tsv, nv, tnv, ragged);
+  if (j == nt - 2) {
+    iteration(j, ragged);
     ++j;
-    take_next();
-    if (needs_rescale(st, mt)) rescale_acc(apply_rescale(st, mt));
+    if (needs_rescale()) rescale();
   }
   {  // drain: the last tile's probabilities and products
     Probs pr;
-    float pe = 0.0f, qe = 0.0f;
-    static_for<0, 32>([&](auto ie) { element(ie, sv, tsv, pr, pe, qe); });
-    products(smem + (j & 1) * C::kStage, pr, [](auto) {});
+    all_steps(IC<0>{}, IC<32>{}, IC<4>{}, [&](auto is, auto ie) { elem_step(is, ie, pr); });
+    bf16x8 vf[C::kBlocksD], tvf[C::kBlocksD];
+    load_v0(smem + (j & 1) * C::kStage, vf, tvf);
+    products(smem + (j & 1) * C::kStage, pr, vf, tvf, [](auto) {});
   }
 
   // ---- epilogue ------------------------------------------------------------
