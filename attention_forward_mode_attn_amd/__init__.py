@@ -2,7 +2,9 @@
 
 The functions below carry the C ABI's names and only marshal arguments; every
 step of the computation runs in the HIP kernels of the library.  ``fwd`` is a
-convenience wrapper that allocates the outputs with torch and raises on error.
+convenience wrapper that allocates the outputs with torch and raises on error;
+``fwd_part``, ``merge`` and ``fwd_split`` do the same for the key-sharded
+partial passes and their exact merge.
 There is no fallback: if the library is missing, every call raises.
 """
 from __future__ import annotations
@@ -12,19 +14,22 @@ import os
 
 __all__ = [
     "ATTN_JVP_FP32", "ATTN_JVP_BF16", "ATTN_JVP_OK", "ATTN_JVP_EINVAL", "ATTN_JVP_EUNSUPPORTED",
-    "ATTN_JVP_EALIGN", "ATTN_JVP_ELAUNCH", "AttnJvpError", "attn_jvp_fwd", "attn_jvp_status_string",
-    "attn_jvp_last_error", "attn_jvp_version", "fwd", "library_path", "load_library",
+    "ATTN_JVP_EALIGN", "ATTN_JVP_ELAUNCH", "ATTN_JVP_MAX_MERGE_PARTS", "AttnJvpError", "attn_jvp_fwd",
+    "attn_jvp_fwd_part", "attn_jvp_merge", "attn_jvp_status_string", "attn_jvp_last_error",
+    "attn_jvp_version", "fwd", "fwd_part", "merge", "fwd_split", "shard_bounds", "library_path",
+    "load_library",
 ]
 
 ATTN_JVP_FP32, ATTN_JVP_BF16 = 0, 1
 ATTN_JVP_OK, ATTN_JVP_EINVAL, ATTN_JVP_EUNSUPPORTED, ATTN_JVP_EALIGN, ATTN_JVP_ELAUNCH = 0, 1, 2, 3, 4
+ATTN_JVP_MAX_MERGE_PARTS = 16
 
 _LIB = None
 
 
 class AttnJvpError(RuntimeError):
     def __init__(self, status: int, detail: str):
-        super().__init__(f"attn_jvp_fwd failed: {attn_jvp_status_string(status)} ({status}): {detail}")
+        super().__init__(f"attn_jvp call failed: {attn_jvp_status_string(status)} ({status}): {detail}")
         self.status = status
 
 
@@ -49,6 +54,10 @@ def load_library() -> ctypes.CDLL:
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.attn_jvp_fwd.argtypes = [vp] * 9 + [i64] * 5 + [ctypes.c_float, ctypes.c_int, vp]
     lib.attn_jvp_fwd.restype = ctypes.c_int
+    lib.attn_jvp_fwd_part.argtypes = [vp] * 10 + [i64] * 6 + [ctypes.c_float, ctypes.c_int, vp]
+    lib.attn_jvp_fwd_part.restype = ctypes.c_int
+    lib.attn_jvp_merge.argtypes = [ctypes.c_int] + [ctypes.POINTER(vp)] * 4 + [vp] * 4 + [i64] * 2 + [ctypes.c_int, vp]
+    lib.attn_jvp_merge.restype = ctypes.c_int
     lib.attn_jvp_status_string.argtypes = [ctypes.c_int]
     lib.attn_jvp_status_string.restype = ctypes.c_char_p
     lib.attn_jvp_last_error.argtypes = []
@@ -78,6 +87,34 @@ def attn_jvp_fwd(q, k, v, tq, tk, tv, o, to, lse, B, H, Lq, Lk, d, scale, dtype,
     ))
 
 
+def attn_jvp_fwd_part(q, k, v, tq, tk, tv, o, to, lse, tlse, B, H, Lq, Lk, kv_rows, d, scale, dtype,
+                      stream=None) -> int:
+    """Marshal to the C entry point (arguments as ``attn_jvp_fwd``; ``tlse``
+    may be None).  Returns the status code."""
+    lib = load_library()
+    return int(lib.attn_jvp_fwd_part(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv), _ptr(o), _ptr(to), _ptr(lse), _ptr(tlse),
+        int(B), int(H), int(Lq), int(Lk), int(kv_rows), int(d), float(scale), int(dtype), stream,
+    ))
+
+
+def attn_jvp_merge(n, o_parts, to_parts, lse_parts, tlse_parts, o, to, lse, tlse, rows, d, dtype,
+                   stream=None) -> int:
+    """Marshal to the C entry point; the four part lists hold n tensors or
+    device addresses each (None entries become NULL).  Returns the status code."""
+    lib = load_library()
+
+    def arr(xs):
+        if xs is None:
+            return None
+        return (ctypes.c_void_p * max(len(xs), 1))(*[_ptr(x) for x in xs])
+
+    return int(lib.attn_jvp_merge(
+        int(n), arr(o_parts), arr(to_parts), arr(lse_parts), arr(tlse_parts),
+        _ptr(o), _ptr(to), _ptr(lse), _ptr(tlse), int(rows), int(d), int(dtype), stream,
+    ))
+
+
 def attn_jvp_status_string(status: int) -> str:
     return load_library().attn_jvp_status_string(int(status)).decode()
 
@@ -97,17 +134,9 @@ def fwd(q, k, v, tq, tk, tv, scale=None, out=None, stream=None):
     torch.cuda.Stream) or the current stream."""
     import torch
 
-    ins = (q, k, v, tq, tk, tv)
-    dt = q.dtype
-    if dt not in (torch.float32, torch.bfloat16):
-        raise TypeError("q must be float32 or bfloat16")
-    for x in ins:
-        if x.dtype != dt or x.device != q.device or not x.is_contiguous() or x.dim() != 4:
-            raise ValueError("all inputs: same dtype and device, contiguous, 4-D [B,H,L,d]")
+    dtype = _check_inputs(q, k, v, tq, tk, tv)
     B, H, Lq, d = q.shape
     Lk = k.shape[2]
-    if tq.shape != q.shape or any(x.shape != (B, H, Lk, d) for x in (k, v, tk, tv)):
-        raise ValueError("shape mismatch: q, tq [B,H,Lq,d]; k, v, tk, tv [B,H,Lk,d]")
     if scale is None:
         scale = d ** -0.5
     if out is None:
@@ -117,8 +146,104 @@ def fwd(q, k, v, tq, tk, tv, scale=None, out=None, stream=None):
     else:
         o, to, lse = out
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
-    status = attn_jvp_fwd(q, k, v, tq, tk, tv, o, to, lse, B, H, Lq, Lk, d, scale,
-                          ATTN_JVP_BF16 if dt == torch.bfloat16 else ATTN_JVP_FP32, s.cuda_stream)
+    status = attn_jvp_fwd(q, k, v, tq, tk, tv, o, to, lse, B, H, Lq, Lk, d, scale, dtype, s.cuda_stream)
     if status != ATTN_JVP_OK:
         raise AttnJvpError(status, attn_jvp_last_error())
     return o, to, lse
+
+
+def _check_inputs(q, k, v, tq, tk, tv):
+    import torch
+
+    dt = q.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("q must be float32 or bfloat16")
+    for x in (q, k, v, tq, tk, tv):
+        if x.dtype != dt or x.device != q.device or not x.is_contiguous() or x.dim() != 4:
+            raise ValueError("all inputs: same dtype and device, contiguous, 4-D [B,H,L,d]")
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    if tq.shape != q.shape or any(x.shape != (B, H, Lk, d) for x in (k, v, tk, tv)):
+        raise ValueError("shape mismatch: q, tq [B,H,Lq,d]; k, v, tk, tv [B,H,Lk,d]")
+    return ATTN_JVP_BF16 if dt == torch.bfloat16 else ATTN_JVP_FP32
+
+
+def fwd_part(q, k, v, tq, tk, tv, k0, k1, scale=None, out=None, stream=None):
+    """O, tO, lse, tlse of the keys [k0, k1) of k, v, tk, tv (torch tensors as
+    in ``fwd``): the partial result of one key shard.  The shard is addressed
+    in place (no copy).  ``out=(o, to, lse, tlse)`` reuses buffers."""
+    import torch
+
+    dtype = _check_inputs(q, k, v, tq, tk, tv)
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    if not 0 <= k0 < k1 <= Lk:
+        raise ValueError("need 0 <= k0 < k1 <= Lk")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        o, to = torch.empty_like(q), torch.empty_like(q)
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+        tlse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    else:
+        o, to, lse, tlse = out
+    off = k0 * d * k.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    status = attn_jvp_fwd_part(q, k.data_ptr() + off, v.data_ptr() + off, tq, tk.data_ptr() + off,
+                               tv.data_ptr() + off, o, to, lse, tlse, B, H, Lq, k1 - k0, Lk, d, scale, dtype,
+                               s.cuda_stream)
+    if status != ATTN_JVP_OK:
+        raise AttnJvpError(status, attn_jvp_last_error())
+    return o, to, lse, tlse
+
+
+def merge(parts, out=None, stream=None):
+    """Exact merge of partial results ``parts`` = [(o, to, lse, tlse), ...]
+    over disjoint key shards; returns (o, to, lse, tlse) of the union."""
+    import torch
+
+    if not 1 <= len(parts) <= ATTN_JVP_MAX_MERGE_PARTS:
+        raise ValueError(f"1 .. {ATTN_JVP_MAX_MERGE_PARTS} parts")
+    o0 = parts[0][0]
+    dtype = ATTN_JVP_BF16 if o0.dtype == torch.bfloat16 else ATTN_JVP_FP32
+    d = o0.shape[-1]
+    rows = o0.numel() // d
+    for o, to, lse, tlse in parts:
+        if o.shape != o0.shape or to.shape != o0.shape or o.dtype != o0.dtype or to.dtype != o0.dtype:
+            raise ValueError("all parts: o and to of one shape and dtype")
+        if lse.numel() != rows or tlse.numel() != rows or lse.dtype != torch.float32 or tlse.dtype != torch.float32:
+            raise ValueError("all parts: lse and tlse float32 with one value per row")
+        if not all(x.is_contiguous() for x in (o, to, lse, tlse)):
+            raise ValueError("all parts contiguous")
+    if out is None:
+        o, to = torch.empty_like(o0), torch.empty_like(o0)
+        lse, tlse = torch.empty_like(parts[0][2]), torch.empty_like(parts[0][3])
+    else:
+        o, to, lse, tlse = out
+    s = stream if stream is not None else torch.cuda.current_stream(o0.device)
+    status = attn_jvp_merge(len(parts), [p[0] for p in parts], [p[1] for p in parts], [p[2] for p in parts],
+                            [p[3] for p in parts], o, to, lse, tlse, rows, d, dtype, s.cuda_stream)
+    if status != ATTN_JVP_OK:
+        raise AttnJvpError(status, attn_jvp_last_error())
+    return o, to, lse, tlse
+
+
+def shard_bounds(Lk: int, n: int, align: int = 64):
+    """Split [0, Lk) into n contiguous non-empty shards, boundaries on multiples
+    of ``align`` where the length allows."""
+    if not 1 <= n <= Lk:
+        raise ValueError("need 1 <= n <= Lk")
+    units = -(-Lk // align)
+    if units >= n:
+        cuts = [min(Lk, (i * units // n) * align) for i in range(n + 1)]
+    else:
+        cuts = [i * Lk // n for i in range(n + 1)]
+    return [(cuts[i], cuts[i + 1]) for i in range(n)]
+
+
+def fwd_split(q, k, v, tq, tk, tv, n_split, scale=None, stream=None):
+    """The attention-JVP computed as ``n_split`` key shards and merged:
+    returns (o, to, lse, tlse), equal to ``fwd`` (plus tlse) up to rounding."""
+    parts = [fwd_part(q, k, v, tq, tk, tv, a, b, scale=scale, stream=stream)
+             for a, b in shard_bounds(k.shape[2], n_split)]
+    return merge(parts, stream=stream)

@@ -9,6 +9,8 @@
 #include "attn_jvp.h"
 #include "launch.h"
 
+static_assert(ATTN_JVP_MAX_MERGE_PARTS == attnjvp::kMaxMergeParts, "merge part limit");
+
 namespace {
 
 thread_local char g_last_error[256] = "";
@@ -39,34 +41,100 @@ const char* attn_jvp_status_string(int status) {
 
 const char* attn_jvp_last_error(void) { return g_last_error; }
 
-int attn_jvp_fwd(const void* q, const void* k, const void* v, const void* tq, const void* tk, const void* tv,
-                 void* o, void* to, float* lse, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
-                 float scale, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int fwd_impl(const void* q, const void* k, const void* v, const void* tq, const void* tk, const void* tv, void* o,
+             void* to, float* lse, float* tlse, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t kv_rows,
+             int64_t d, float scale, int dtype, void* stream) {
   g_last_error[0] = '\0';
   if (dtype != ATTN_JVP_FP32 && dtype != ATTN_JVP_BF16) return fail(ATTN_JVP_EINVAL, "dtype must be 0 (fp32) or 1 (bf16)");
   if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || d < 0) return fail(ATTN_JVP_EINVAL, "negative size");
   if (d != 64 && d != 128) return fail(ATTN_JVP_EUNSUPPORTED, "head dimension must be 64 or 128");
   if (B == 0 || H == 0 || Lq == 0) return ATTN_JVP_OK;  // nothing to compute
   if (Lk == 0) return fail(ATTN_JVP_EINVAL, "Lk == 0: softmax over no keys");
+  if (kv_rows < Lk) return fail(ATTN_JVP_EINVAL, "kv_rows < Lk");
   if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(ATTN_JVP_EINVAL, "scale must be finite and > 0");
   if (!q || !k || !v || !tq || !tk || !tv || !o || !to || !lse) return fail(ATTN_JVP_EINVAL, "NULL pointer");
   const void* t16[] = {q, k, v, tq, tk, tv, o, to};
   for (const void* x : t16)
     if (!aligned(x, 16)) return fail(ATTN_JVP_EALIGN, "tensor pointers must be 16-byte aligned");
-  if (!aligned(lse, 4)) return fail(ATTN_JVP_EALIGN, "lse must be 4-byte aligned");
+  if (!aligned(lse, 4) || !aligned(tlse, 4)) return fail(ATTN_JVP_EALIGN, "lse and tlse must be 4-byte aligned");
   const int64_t lim = int64_t(1) << 29;  // elements per head: keeps byte offsets within 32 bits
   if (Lq * d >= lim || Lk * d >= lim) return fail(ATTN_JVP_EUNSUPPORTED, "sequence too long for one head");
+  if (kv_rows > INT32_MAX) return fail(ATTN_JVP_EUNSUPPORTED, "kv_rows too large");
   const int64_t qtiles = (Lq + 127) / 128;
   if (B > INT32_MAX || H > INT32_MAX || B * H > INT32_MAX || B * H * qtiles >= (int64_t(1) << 31))
     return fail(ATTN_JVP_EUNSUPPORTED, "too many workgroups");
 
   attnjvp::Problem p;
   p.q = q; p.k = k; p.v = v; p.tq = tq; p.tk = tk; p.tv = tv;
-  p.o = o; p.to = to; p.lse = lse;
+  p.o = o; p.to = to; p.lse = lse; p.tlse = tlse;
   p.B = (int)B; p.H = (int)H; p.Lq = (int)Lq; p.Lk = (int)Lk; p.d = (int)d;
+  p.kv_rows = (int)kv_rows;
   p.scale = scale;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = dtype == ATTN_JVP_BF16 ? attnjvp::launch_bf16(p, s) : attnjvp::launch_fp32(p, s);
+  if (e != hipSuccess) {
+    std::snprintf(g_last_error, sizeof g_last_error, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+    return ATTN_JVP_ELAUNCH;
+  }
+  return ATTN_JVP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_jvp_fwd(const void* q, const void* k, const void* v, const void* tq, const void* tk, const void* tv,
+                 void* o, void* to, float* lse, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
+                 float scale, int dtype, void* stream) {
+  return fwd_impl(q, k, v, tq, tk, tv, o, to, lse, nullptr, B, H, Lq, Lk, Lk, d, scale, dtype, stream);
+}
+
+int attn_jvp_fwd_part(const void* q, const void* k, const void* v, const void* tq, const void* tk,
+                      const void* tv, void* o, void* to, float* lse, float* tlse, int64_t B, int64_t H,
+                      int64_t Lq, int64_t Lk, int64_t kv_rows, int64_t d, float scale, int dtype,
+                      void* stream) {
+  return fwd_impl(q, k, v, tq, tk, tv, o, to, lse, tlse, B, H, Lq, Lk, kv_rows, d, scale, dtype, stream);
+}
+
+int attn_jvp_merge(int n, const void* const* o_parts, const void* const* to_parts, const float* const* lse_parts,
+                   const float* const* tlse_parts, void* o, void* to, float* lse, float* tlse, int64_t rows,
+                   int64_t d, int dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (dtype != ATTN_JVP_FP32 && dtype != ATTN_JVP_BF16) return fail(ATTN_JVP_EINVAL, "dtype must be 0 (fp32) or 1 (bf16)");
+  if (n < 1 || n > ATTN_JVP_MAX_MERGE_PARTS) return fail(ATTN_JVP_EINVAL, "n must be in 1 .. ATTN_JVP_MAX_MERGE_PARTS");
+  if (rows < 0 || d < 0) return fail(ATTN_JVP_EINVAL, "negative size");
+  if (d != 64 && d != 128) return fail(ATTN_JVP_EUNSUPPORTED, "head dimension must be 64 or 128");
+  if (rows == 0) return ATTN_JVP_OK;
+  if (rows / (256 / (d / 8)) >= INT32_MAX) return fail(ATTN_JVP_EUNSUPPORTED, "too many rows");
+  if (!o_parts || !to_parts || !lse_parts || !tlse_parts || !o || !to || !lse)
+    return fail(ATTN_JVP_EINVAL, "NULL pointer");
+  attnjvp::MergeProblem p{};
+  p.n = n;
+  for (int s = 0; s < n; ++s) {
+    if (!o_parts[s] || !to_parts[s] || !lse_parts[s] || !tlse_parts[s]) return fail(ATTN_JVP_EINVAL, "NULL pointer");
+    if (!aligned(o_parts[s], 16) || !aligned(to_parts[s], 16))
+      return fail(ATTN_JVP_EALIGN, "tensor pointers must be 16-byte aligned");
+    if (!aligned(lse_parts[s], 4) || !aligned(tlse_parts[s], 4))
+      return fail(ATTN_JVP_EALIGN, "lse and tlse must be 4-byte aligned");
+    p.o[s] = o_parts[s];
+    p.to[s] = to_parts[s];
+    p.lse[s] = lse_parts[s];
+    p.tlse[s] = tlse_parts[s];
+  }
+  if (!aligned(o, 16) || !aligned(to, 16)) return fail(ATTN_JVP_EALIGN, "tensor pointers must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(tlse, 4)) return fail(ATTN_JVP_EALIGN, "lse and tlse must be 4-byte aligned");
+  p.out_o = o;
+  p.out_to = to;
+  p.out_lse = lse;
+  p.out_tlse = tlse;
+  p.rows = rows;
+  p.d = (int)d;
+  p.bf16 = dtype == ATTN_JVP_BF16;
+  const hipError_t e = attnjvp::launch_merge(p, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     std::snprintf(g_last_error, sizeof g_last_error, "HIP error %d: %s", (int)e, hipGetErrorString(e));
     return ATTN_JVP_ELAUNCH;

@@ -27,7 +27,8 @@ struct Params {
   void* o;
   void* to;
   float* lse;
-  int Lq, Lk, n_qtiles, n_blocks;
+  float* tlse;
+  int Lq, Lk, kv_rows, n_qtiles, n_blocks;
   float scale;
 };
 
@@ -95,7 +96,7 @@ void attn_jvp_fp32_kernel(Params p) {
   const int bh = blk / p.n_qtiles, qt = blk % p.n_qtiles;
   const int Lq = p.Lq, Lk = p.Lk;
 
-  const size_t qhead = (size_t)bh * Lq * D * 4, khead = (size_t)bh * Lk * D * 4;
+  const size_t qhead = (size_t)bh * Lq * D * 4, khead = (size_t)bh * p.kv_rows * D * 4;
   const uint32_t qbytes = (uint32_t)Lq * D * 4, kbytes = (uint32_t)Lk * D * 4;
   const auto rq = make_rsrc((const char*)p.q + qhead, qbytes);
   const auto rtq = make_rsrc((const char*)p.tq + qhead, qbytes);
@@ -245,6 +246,10 @@ void attn_jvp_fp32_kernel(Params p) {
   if (hh == 0) {
     const auto rl = make_rsrc((const char*)p.lse + (size_t)bh * Lq * 4, (uint32_t)Lq * 4);
     buf_store4(rl, (uint32_t)qrow * 4, (st.m + __builtin_amdgcn_logf(l)) * kLn2);
+    if (p.tlse) {
+      const auto rtl = make_rsrc((const char*)p.tlse + (size_t)bh * Lq * 4, (uint32_t)Lq * 4);
+      buf_store4(rtl, (uint32_t)qrow * 4, mu);
+    }
   }
 }
 
@@ -252,8 +257,8 @@ template <int D>
 hipError_t launch(const Problem& pr, hipStream_t stream) {
   Params p;
   p.q = pr.q; p.k = pr.k; p.v = pr.v; p.tq = pr.tq; p.tk = pr.tk; p.tv = pr.tv;
-  p.o = pr.o; p.to = pr.to; p.lse = pr.lse;
-  p.Lq = pr.Lq; p.Lk = pr.Lk; p.scale = pr.scale;
+  p.o = pr.o; p.to = pr.to; p.lse = pr.lse; p.tlse = pr.tlse;
+  p.Lq = pr.Lq; p.Lk = pr.Lk; p.kv_rows = pr.kv_rows; p.scale = pr.scale;
   p.n_qtiles = (pr.Lq + kBlockRows - 1) / kBlockRows;
   p.n_blocks = pr.B * pr.H * p.n_qtiles;
   hipLaunchKernelGGL(attn_jvp_fp32_kernel<D>, dim3(p.n_blocks), dim3(kThreads), 0, stream, p);

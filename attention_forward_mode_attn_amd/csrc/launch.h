@@ -14,12 +14,33 @@ struct Problem {
   void* o;
   void* to;
   float* lse;
+  float* tlse;  // may be null (not written)
   int B, H, Lq, Lk, d;
+  int kv_rows;  // rows between consecutive K/V heads in memory (>= Lk)
   float scale;
 };
 
 // Both assume validated arguments (see the C ABI) and B*H*Lq > 0, Lk > 0.
 hipError_t launch_bf16(const Problem& p, hipStream_t stream);
 hipError_t launch_fp32(const Problem& p, hipStream_t stream);
+
+constexpr int kMaxMergeParts = 16;
+
+struct MergeProblem {
+  int n;  // 1 .. kMaxMergeParts
+  const void* o[kMaxMergeParts];
+  const void* to[kMaxMergeParts];
+  const float* lse[kMaxMergeParts];
+  const float* tlse[kMaxMergeParts];
+  void* out_o;
+  void* out_to;
+  float* out_lse;
+  float* out_tlse;  // may be null
+  int64_t rows;     // > 0
+  int d;            // 64 or 128
+  bool bf16;
+};
+
+hipError_t launch_merge(const MergeProblem& p, hipStream_t stream);
 
 }  // namespace attnjvp

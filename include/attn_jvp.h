@@ -34,7 +34,10 @@
 extern "C" {
 #endif
 
-#define ATTN_JVP_VERSION 10000 /* 1.0.0 */
+#define ATTN_JVP_VERSION 10100 /* 1.1.0 */
+
+/* Largest number of partial results one attn_jvp_merge call combines. */
+#define ATTN_JVP_MAX_MERGE_PARTS 16
 
 /* Element type of q, k, v, tq, tk, tv, o and to (lse is always float32). */
 typedef enum {
@@ -91,6 +94,65 @@ int attn_jvp_fwd(const void* q, const void* k, const void* v,
                  void* o, void* to, float* lse,
                  int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t d,
                  float scale, int dtype, void* stream);
+
+/*
+ * attn_jvp_fwd_part — attn_jvp_fwd over one shard of the keys, returning the
+ * partial state that attn_jvp_merge combines exactly.
+ *
+ * The pages describe the fused kernel as usable under context parallelism,
+ * with the tangents of Q, K and V distributed like Q, K and V themselves
+ * (ai.info summary of "Large Scale Diffusion Distillation via Score-Regularized
+ * Continuous-Time Consistency", "Methodology in Plain English"; papernotes.org
+ * notes, "Key designs" item 1).  With the keys split over shards, each shard's
+ * softmax-normalised result is a complete description of its keys once the
+ * tangent of its log-sum-exp is kept as well:
+ *
+ *   tlse = d/dt lse = sum_j P_ij tS_ij     (mu above; natural-log units)
+ *
+ * Arguments are those of attn_jvp_fwd, plus
+ *   k, tk, v, tv   point at the first key row of the shard in [B, H, kv_rows, d]
+ *                  tensors: head (b, h) of the shard starts (b*H + h)*kv_rows*d
+ *                  elements after the pointer, and its Lk rows are used
+ *   kv_rows        rows per head of the K/V tensors in memory, >= Lk, < 2^31
+ *   tlse [B, H, Lq] float32, written with mu; may be NULL (then not written)
+ * With kv_rows == Lk and tlse == NULL this is attn_jvp_fwd.
+ * Errors: as attn_jvp_fwd; kv_rows < Lk is ATTN_JVP_EINVAL.
+ */
+int attn_jvp_fwd_part(const void* q, const void* k, const void* v,
+                      const void* tq, const void* tk, const void* tv,
+                      void* o, void* to, float* lse, float* tlse,
+                      int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t kv_rows, int64_t d,
+                      float scale, int dtype, void* stream);
+
+/*
+ * attn_jvp_merge — exact merge of n results over disjoint key shards.
+ *
+ * For each of `rows` query rows (B*H*Lq for [B, H, Lq, d] tensors), with the
+ * shard results (O_s, tO_s, lse_s, tlse_s) of attn_jvp_fwd_part:
+ *   lse  = log sum_s exp(lse_s),      w_s = exp(lse_s - lse)
+ *   O    = sum_s w_s O_s
+ *   tlse = sum_s w_s tlse_s
+ *   tO   = sum_s w_s (tO_s + (tlse_s - tlse) O_s)
+ * which is the attention-JVP over the union of the shards' keys (up to
+ * rounding; bf16 partials carry their own bf16 rounding into the merge).
+ *
+ * Arguments
+ *   n                      number of shards, 1 .. ATTN_JVP_MAX_MERGE_PARTS
+ *   o_parts, to_parts      host arrays of n device pointers, [rows, d] each, dtype
+ *   lse_parts, tlse_parts  host arrays of n device pointers, [rows] float32 each
+ *   o, to                  [rows, d] outputs (device, written)
+ *   lse                    [rows] float32 output (device, written)
+ *   tlse                   [rows] float32 output, may be NULL (then not written)
+ *   rows, d                d in {64, 128}
+ *   dtype, stream          as attn_jvp_fwd (arithmetic is float32)
+ * Ownership, alignment (16 bytes for [rows, d] tensors, 4 for [rows]),
+ * execution and errors follow attn_jvp_fwd; rows == 0 is a no-op; outputs must
+ * not overlap any input.  The host arrays are read during the call only.
+ */
+int attn_jvp_merge(int n, const void* const* o_parts, const void* const* to_parts,
+                   const float* const* lse_parts, const float* const* tlse_parts,
+                   void* o, void* to, float* lse, float* tlse,
+                   int64_t rows, int64_t d, int dtype, void* stream);
 
 /* Static description of a status code ("unknown status" for others). */
 const char* attn_jvp_status_string(int status);

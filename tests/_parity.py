@@ -33,16 +33,18 @@ def lse_err(x, ref) -> float:
     return float(np.max(np.abs(x - ref) / np.maximum(1.0, np.abs(ref)))) if ref.size else 0.0
 
 
-def oracle_head(w, b, h, rows=None):
+def oracle_head(w, b, h, rows=None, with_tlse=False):
     a = {t: head_array(w, t, b, h) for t in TENSORS}
-    return attention_jvp_head(a["q"], a["k"], a["v"], a["tq"], a["tk"], a["tv"], w.scale, rows=rows)
+    return attention_jvp_head(a["q"], a["k"], a["v"], a["tq"], a["tk"], a["tv"], w.scale, rows=rows,
+                              with_tlse=with_tlse)
 
 
-def compare(w, o, to, lse, rows_fn=None, threads=8):
+def compare(w, o, to, lse, rows_fn=None, threads=8, tlse=None):
     """Errors of device outputs against the oracle, over all heads.
 
     rows_fn(b, h) -> row indices to check (None: all rows).  Returns a dict with
-    the global normalised errors and per-head errors of tO.
+    the global normalised errors and per-head errors of tO; with ``tlse`` (the
+    device's tangent of lse) also its normalised error "tlse".
     """
     import torch
 
@@ -51,15 +53,15 @@ def compare(w, o, to, lse, rows_fn=None, threads=8):
     def one(bh):
         b, h = bh
         rows = rows_fn(b, h) if rows_fn else None
-        O, tO, L = oracle_head(w, b, h, rows)
-        return bh, rows, O, tO, L
+        O, tO, L, M = oracle_head(w, b, h, rows, with_tlse=True)
+        return bh, rows, O, tO, L, M
 
-    dO = dT = 0.0
-    maxO = maxT = 0.0
+    dO = dT = dM = 0.0
+    maxO = maxT = maxM = 0.0
     lse_e = 0.0
     per_head = {}
     with ThreadPoolExecutor(threads) as ex:
-        for (b, h), rows, O, tO, L in ex.map(one, heads):
+        for (b, h), rows, O, tO, L, M in ex.map(one, heads):
             idx = torch.as_tensor(rows, device=o.device) if rows is not None else None
             go = (o[b, h] if idx is None else o[b, h].index_select(0, idx)).float().cpu().numpy()
             gt = (to[b, h] if idx is None else to[b, h].index_select(0, idx)).float().cpu().numpy()
@@ -70,9 +72,16 @@ def compare(w, o, to, lse, rows_fn=None, threads=8):
             maxT = max(maxT, float(np.max(np.abs(tO))))
             lse_e = max(lse_e, lse_err(gl, L))
             per_head[(b, h)] = (norm_err(go, O), norm_err(gt, tO))
-    return {
+            if tlse is not None:
+                gm = (tlse[b, h] if idx is None else tlse[b, h].index_select(0, idx)).cpu().numpy()
+                dM = max(dM, float(np.max(np.abs(gm - M))))
+                maxM = max(maxM, float(np.max(np.abs(M))))
+    res = {
         "O": dO / max(maxO, 1e-300),
         "tO": dT / max(maxT, 1e-300),
         "lse": lse_e,
         "per_head": per_head,
     }
+    if tlse is not None:
+        res["tlse"] = dM / max(maxM, 1e-300)
+    return res

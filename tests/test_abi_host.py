@@ -30,13 +30,14 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert names == ["attn_jvp_fwd", "attn_jvp_last_error", "attn_jvp_status_string", "attn_jvp_version"]
+    assert names == ["attn_jvp_fwd", "attn_jvp_fwd_part", "attn_jvp_last_error", "attn_jvp_merge",
+                     "attn_jvp_status_string", "attn_jvp_version"]
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert A.attn_jvp_version() == 10000
+    assert A.attn_jvp_version() == 10100
     assert A.attn_jvp_status_string(0) == "ok"
     assert A.attn_jvp_status_string(A.ATTN_JVP_EUNSUPPORTED).startswith("unsupported")
     assert A.attn_jvp_status_string(99) == "unknown status"
@@ -113,3 +114,65 @@ def test_no_device_returns_launch_error(lib):
 def test_ctypes_signature_is_c_abi(lib):
     assert lib.attn_jvp_fwd.restype is ctypes.c_int
     assert len(lib.attn_jvp_fwd.argtypes) == 17
+    assert len(lib.attn_jvp_fwd_part.argtypes) == 19
+    assert len(lib.attn_jvp_merge.argtypes) == 13
+
+
+def test_merge_part_limit_matches_header():
+    src = open(HEADER).read()
+    assert re.search(r"#define ATTN_JVP_MAX_MERGE_PARTS (\d+)", src).group(1) == str(A.ATTN_JVP_MAX_MERGE_PARTS)
+
+
+def call_part(Lk=8, kv_rows=8, tlse=None, **kw):
+    p = [FAKE] * 9
+    return A.attn_jvp_fwd_part(*p, FAKE if tlse is None else tlse, kw.get("B", 1), 1, 8, Lk, kv_rows,
+                               kw.get("d", 64), 0.125, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Lk=8, kv_rows=7), A.ATTN_JVP_EINVAL),
+    (dict(Lk=8, kv_rows=1 << 31), A.ATTN_JVP_EUNSUPPORTED),
+    (dict(tlse=FAKE + 1), A.ATTN_JVP_EALIGN),
+    (dict(d=32), A.ATTN_JVP_EUNSUPPORTED),
+])
+def test_fwd_part_rejects_invalid_arguments(lib, kw, status):
+    assert call_part(**kw) == status
+    assert A.attn_jvp_last_error() != ""
+
+
+def call_merge(n=2, parts=None, out=None, rows=16, d=64, dtype=1):
+    parts = parts if parts is not None else [[FAKE] * n for _ in range(4)]
+    out = out if out is not None else [FAKE] * 4
+    return A.attn_jvp_merge(n, *parts, *out, rows, d, dtype)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=0), A.ATTN_JVP_EINVAL),
+    (dict(n=17), A.ATTN_JVP_EINVAL),
+    (dict(dtype=3), A.ATTN_JVP_EINVAL),
+    (dict(rows=-1), A.ATTN_JVP_EINVAL),
+    (dict(d=100), A.ATTN_JVP_EUNSUPPORTED),
+    (dict(parts=[[FAKE, FAKE], [FAKE, 0], [FAKE, FAKE], [FAKE, FAKE]]), A.ATTN_JVP_EINVAL),
+    (dict(parts=[[FAKE, FAKE], [FAKE, FAKE], [FAKE, FAKE], None]), A.ATTN_JVP_EINVAL),
+    (dict(out=[FAKE, FAKE, 0, FAKE]), A.ATTN_JVP_EINVAL),
+    (dict(parts=[[FAKE, FAKE + 8], [FAKE, FAKE], [FAKE, FAKE], [FAKE, FAKE]]), A.ATTN_JVP_EALIGN),
+    (dict(parts=[[FAKE, FAKE], [FAKE, FAKE], [FAKE, FAKE], [FAKE + 2, FAKE]]), A.ATTN_JVP_EALIGN),
+    (dict(out=[FAKE, FAKE, FAKE, FAKE + 2]), A.ATTN_JVP_EALIGN),
+    (dict(rows=1 << 40), A.ATTN_JVP_EUNSUPPORTED),
+])
+def test_merge_rejects_invalid_arguments(lib, kw, status):
+    assert call_merge(**kw) == status
+    assert A.attn_jvp_last_error() != ""
+
+
+def test_merge_zero_rows_is_ok_without_pointers(lib):
+    assert call_merge(rows=0, parts=[[0, 0]] * 4, out=[0] * 4) == A.ATTN_JVP_OK
+
+
+def test_new_entry_points_report_launch_error_without_device(lib):
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this checks the no-device path only")
+    assert call_part() == A.ATTN_JVP_ELAUNCH
+    assert call_merge() == A.ATTN_JVP_ELAUNCH

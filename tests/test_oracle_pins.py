@@ -9,13 +9,18 @@ differentiation, and a brute-force Jacobian; O and lse by torch's
 scaled_dot_product_attention and scipy's logsumexp; plus closed forms and
 invariants of the tangent map.  The last tests plant plausible mistakes in the
 oracle's outputs and check that the pins reject every one of them.
+
+The tangent of lse (mu, step 5, returned with ``with_tlse``) is pinned by the
+complex-step and finite-difference derivatives of lse; the merge of key-shard
+results (``merge_shards``) by the full-key definition, which the pins above
+fix.
 """
 import numpy as np
 import pytest
 import scipy.special
 import torch
 
-from oracle import attention_jvp, attention_jvp_head
+from oracle import attention_jvp, attention_jvp_head, merge_shards
 
 
 def case(seed, Lq, Lk, d, sig=1.0):
@@ -269,3 +274,61 @@ def test_pins_reject_planted_mistakes():
     for name, (t_bad, l_bad) in _mutants(q, k, v, tq, tk, tv, s).items():
         caught = rel(t_bad, t_cs) > 1e-3 or rel(l_bad, lse_ref) > 1e-3
         assert caught, name
+
+
+@pytest.mark.parametrize("Lq,Lk,d", SHAPES)
+def test_tlse_is_the_tangent_of_lse(Lq, Lk, d):
+    q, k, v, tq, tk, tv = case(21, Lq, Lk, d)
+    s = d ** -0.5
+    _, _, _, mu = attention_jvp_head(q, k, v, tq, tk, tv, s, with_tlse=True)
+    _, l_cs = complex_step(q, k, v, tq, tk, tv, s)
+    assert rel(mu, l_cs) < 1e-13
+    eps = 1e-5
+    lp = plain_forward(q + eps * tq, k + eps * tk, v, s)[1]
+    lm = plain_forward(q - eps * tq, k - eps * tk, v, s)[1]
+    assert rel(mu, (lp - lm) / (2 * eps)) < 1e-7
+
+
+def test_tlse_vanishes_without_logit_tangents():
+    q, k, v, tq, tk, tv = case(22, 5, 7, 4)
+    z = np.zeros_like
+    _, _, _, mu = attention_jvp_head(q, k, v, z(tq), z(tk), tv, 0.5, with_tlse=True)
+    assert np.all(mu == 0.0)
+
+
+SPLITS = [(9, [4, 5]), (33, [1, 32]), (33, [10, 11, 12]), (64, [16, 16, 16, 16]), (7, [1, 1, 5])]
+
+
+@pytest.mark.parametrize("Lk,sizes", SPLITS)
+def test_merge_of_key_shards_is_the_full_result(Lk, sizes):
+    Lq, d = 6, 8
+    q, k, v, tq, tk, tv = case(23, Lq, Lk, d, sig=1.5)
+    s = d ** -0.5
+    full = attention_jvp_head(q, k, v, tq, tk, tv, s, with_tlse=True)
+    cuts = np.concatenate([[0], np.cumsum(sizes)])
+    parts = [attention_jvp_head(q, k[a:b], v[a:b], tq, tk[a:b], tv[a:b], s, with_tlse=True)
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    merged = merge_shards(parts)
+    for got, ref in zip(merged, full):
+        assert rel(got, ref) < 1e-12
+
+
+def test_merge_pins_reject_planted_mistakes():
+    Lq, Lk, d = 6, 12, 8
+    q, k, v, tq, tk, tv = case(24, Lq, Lk, d, sig=1.5)
+    s = d ** -0.5
+    O, tO, lse, mu = attention_jvp_head(q, k, v, tq, tk, tv, s, with_tlse=True)
+    parts = [attention_jvp_head(q, k[a:b], v[a:b], tq, tk[a:b], tv[a:b], s, with_tlse=True)
+             for a, b in ((0, 5), (5, 12))]
+    lse_s = np.stack([p[2] for p in parts])
+    mu_s = np.stack([p[3] for p in parts])
+    w = np.exp(lse_s - lse)
+    mutants = {
+        "no re-centring of the tangent": sum(w[i][:, None] * p[1] for i, p in enumerate(parts)),
+        "equal shard weights": sum(0.5 * (p[1] + (mu_s[i] - mu)[:, None] * p[0]) for i, p in enumerate(parts)),
+        "shift with the wrong sign": sum(w[i][:, None] * (p[1] - (mu_s[i] - mu)[:, None] * p[0])
+                                         for i, p in enumerate(parts)),
+    }
+    assert rel(merge_shards(parts)[1], tO) < 1e-12
+    for name, bad in mutants.items():
+        assert rel(bad, tO) > 1e-3, name
