@@ -129,7 +129,8 @@ def attn_jvp_version() -> int:
 
 def fwd(q, k, v, tq, tk, tv, scale=None, out=None, stream=None):
     """O, tO, lse for torch tensors q, tq [B,H,Lq,d] and k, v, tk, tv [B,H,Lk,d]
-    (contiguous, same device, all float32 or all bfloat16).  Outputs are
+    (contiguous, same device, all float32 or all bfloat16); tk = tv = None is
+    a frozen context (zero key-side tangents, computed without them).  Outputs are
     allocated unless ``out=(o, to, lse)`` is given.  Runs on ``stream`` (a
     torch.cuda.Stream) or the current stream."""
     import torch
@@ -158,12 +159,15 @@ def _check_inputs(q, k, v, tq, tk, tv):
     dt = q.dtype
     if dt not in (torch.float32, torch.bfloat16):
         raise TypeError("q must be float32 or bfloat16")
-    for x in (q, k, v, tq, tk, tv):
+    if (tk is None) != (tv is None):
+        raise ValueError("tk and tv must both be None (frozen context) or both tensors")
+    ins = [x for x in (q, k, v, tq, tk, tv) if x is not None]
+    for x in ins:
         if x.dtype != dt or x.device != q.device or not x.is_contiguous() or x.dim() != 4:
             raise ValueError("all inputs: same dtype and device, contiguous, 4-D [B,H,L,d]")
     B, H, Lq, d = q.shape
     Lk = k.shape[2]
-    if tq.shape != q.shape or any(x.shape != (B, H, Lk, d) for x in (k, v, tk, tv)):
+    if tq.shape != q.shape or any(x.shape != (B, H, Lk, d) for x in ins[1:] if x is not tq):
         raise ValueError("shape mismatch: q, tq [B,H,Lq,d]; k, v, tk, tv [B,H,Lk,d]")
     return ATTN_JVP_BF16 if dt == torch.bfloat16 else ATTN_JVP_FP32
 
@@ -189,9 +193,10 @@ def fwd_part(q, k, v, tq, tk, tv, k0, k1, scale=None, out=None, stream=None):
         o, to, lse, tlse = out
     off = k0 * d * k.element_size()
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
-    status = attn_jvp_fwd_part(q, k.data_ptr() + off, v.data_ptr() + off, tq, tk.data_ptr() + off,
-                               tv.data_ptr() + off, o, to, lse, tlse, B, H, Lq, k1 - k0, Lk, d, scale, dtype,
-                               s.cuda_stream)
+    tk_p = None if tk is None else tk.data_ptr() + off
+    tv_p = None if tv is None else tv.data_ptr() + off
+    status = attn_jvp_fwd_part(q, k.data_ptr() + off, v.data_ptr() + off, tq, tk_p, tv_p, o, to, lse, tlse,
+                               B, H, Lq, k1 - k0, Lk, d, scale, dtype, s.cuda_stream)
     if status != ATTN_JVP_OK:
         raise AttnJvpError(status, attn_jvp_last_error())
     return o, to, lse, tlse

@@ -56,7 +56,8 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* tq, const 
   if (Lk == 0) return fail(ATTN_JVP_EINVAL, "Lk == 0: softmax over no keys");
   if (kv_rows < Lk) return fail(ATTN_JVP_EINVAL, "kv_rows < Lk");
   if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(ATTN_JVP_EINVAL, "scale must be finite and > 0");
-  if (!q || !k || !v || !tq || !tk || !tv || !o || !to || !lse) return fail(ATTN_JVP_EINVAL, "NULL pointer");
+  if (!q || !k || !v || !tq || !o || !to || !lse) return fail(ATTN_JVP_EINVAL, "NULL pointer");
+  if ((tk == nullptr) != (tv == nullptr)) return fail(ATTN_JVP_EINVAL, "tk and tv must both be NULL or both non-NULL");
   const void* t16[] = {q, k, v, tq, tk, tv, o, to};
   for (const void* x : t16)
     if (!aligned(x, 16)) return fail(ATTN_JVP_EALIGN, "tensor pointers must be 16-byte aligned");

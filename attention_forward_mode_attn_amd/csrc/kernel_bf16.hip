@@ -169,7 +169,9 @@ __device__ inline void static_for(F&& f) {
   }
 }
 
-template <int D>
+// kFrozen: the key-side tangents are zero (tK = tV = 0, a frozen context):
+// the tK Q^T and tV P^T products and the tK/tV tile copies are skipped.
+template <int D, bool kFrozen>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_jvp_bf16_kernel(Params p) {
   using C = Cfg<D>;
@@ -190,8 +192,8 @@ void attn_jvp_bf16_kernel(Params p) {
   // the per-lane offset, and rows at or past Lk read as zero.
   const uint32_t kbytes = (uint32_t)Lk * D * 2;
   const __amdgpu_buffer_rsrc_t rkv[4] = {
-      make_rsrc((const char*)p.k + khead, kbytes), make_rsrc((const char*)p.tk + khead, kbytes),
-      make_rsrc((const char*)p.v + khead, kbytes), make_rsrc((const char*)p.tv + khead, kbytes)};
+      make_rsrc((const char*)p.k + khead, kbytes), make_rsrc(kFrozen ? (const char*)p.k : (const char*)p.tk + khead, kFrozen ? 0 : kbytes),
+      make_rsrc((const char*)p.v + khead, kbytes), make_rsrc(kFrozen ? (const char*)p.v : (const char*)p.tv + khead, kFrozen ? 0 : kbytes)};
 
   // Q and tQ fragments (B operand of S^T = K Q^T): lane (n, hh) holds dims
   // 16c + 8hh .. +7 of its query row.  Rows past Lq read as zero.
@@ -232,18 +234,21 @@ void attn_jvp_bf16_kernel(Params p) {
     const uint32_t dst = smem_lds + (j & 1) * C::kStage + tn * C::kTile + (wv * C::kLoadsPerWave + i) * 1024;
     lds_dma16(rkv[tn], dst, (tn < 2 ? voff_k[i] : voff_v[i]) + toff);
   };
+  // tensors copied: K, tK, V, tV (tn = 0..3); K and V only when frozen
+  constexpr int kTensors = kFrozen ? 2 : 4;
+  auto tensor = [](int x) { return kFrozen ? 2 * x : x; };
   auto issue = [&](int j, int tn0) {
 #pragma unroll
-    for (int tn = tn0; tn < tn0 + 2; ++tn)
+    for (int tn = tn0; tn < tn0 + 2; tn += kFrozen ? 2 : 1)
 #pragma unroll
       for (int i = 0; i < C::kLoadsPerWave; ++i) issue_one(j, tn, i);
   };
   // The copies of one pipelined iteration (K|tK of tile j + 2, V|tV of tile
   // j + 1), numbered q = 0 .. kDmaPerIter - 1.
-  constexpr int kDmaPerIter = 4 * C::kLoadsPerWave;
+  constexpr int kDmaPerIter = kTensors * C::kLoadsPerWave;
   auto issue_q = [&](int j, auto iq) {
     constexpr int q = decltype(iq)::value;
-    constexpr int tn = q / C::kLoadsPerWave, i = q % C::kLoadsPerWave;
+    const int tn = tensor(q / C::kLoadsPerWave), i = q % C::kLoadsPerWave;
     issue_one(tn < 2 ? j + 2 : j + 1, tn, i);
   };
 
@@ -255,8 +260,10 @@ void attn_jvp_bf16_kernel(Params p) {
     const uint32_t u = krow + (((2 * c + hh) ^ ksw) << 4);
     kf[0] = *reinterpret_cast<const bf16x8*>(stage + u);
     kf[1] = *reinterpret_cast<const bf16x8*>(stage + 32 * C::kRow + u);
-    kf[2] = *reinterpret_cast<const bf16x8*>(stage + C::kTile + u);
-    kf[3] = *reinterpret_cast<const bf16x8*>(stage + C::kTile + 32 * C::kRow + u);
+    if constexpr (!kFrozen) {
+      kf[2] = *reinterpret_cast<const bf16x8*>(stage + C::kTile + u);
+      kf[3] = *reinterpret_cast<const bf16x8*>(stage + C::kTile + 32 * C::kRow + u);
+    }
   };
   // V fragment via ds_read_b64_tr_b16: in 16-lane group G = lane / 16 (half
   // hh = G / 2, dims 16(G & 1) .. +15 of the 32-dim block), source lane s reads
@@ -284,7 +291,8 @@ void attn_jvp_bf16_kernel(Params p) {
   // key 32 (e / 16) + acc_row(e % 16, hh).
   //
   // S^T = K Q^T and tS^T = K tQ^T + tK Q^T of one 64-key tile, chunk c of the
-  // head dimension: 6 MFMAs (unit u = 0..5).
+  // head dimension: kUPC MFMAs (unit u = 0 .. kUPC - 1; 6, or 4 when frozen).
+  constexpr int kUPC = kFrozen ? 4 : 6;
   auto logit_mfma = [&](auto iu, auto ic, const bf16x8 (&k)[4], f32x16 (&sn)[2], f32x16 (&tsn)[2]) {
     constexpr int u = decltype(iu)::value, c = decltype(ic)::value;
     if constexpr (u == 0) sn[0] = mfma(k[0], qf[c], c == 0 ? f32x16{} : sn[0]);
@@ -389,7 +397,7 @@ void attn_jvp_bf16_kernel(Params p) {
     static_for<0, C::kBlocksD>([&](auto ib) {
       constexpr int b = decltype(ib)::value;
       vf[b] = load_v(stage, 0, b, 0);
-      tvf[b] = load_v(stage, 0, b, 1);
+      if constexpr (!kFrozen) tvf[b] = load_v(stage, 0, b, 1);
     });
   };
   // O^T += V^T P^T and tO^T += tV^T P^T + V^T (P*tS)^T over one tile: 12 MFMAs
@@ -398,6 +406,23 @@ void attn_jvp_bf16_kernel(Params p) {
   // chunk right after their last use.
   auto products = [&](const char* stage, const Probs& pr, bf16x8 (&vf)[C::kBlocksD], bf16x8 (&tvf)[C::kBlocksD],
                       auto&& work) {
+    if constexpr (kFrozen) {
+      // no tV: O^T += V^T P^T and tO^T += V^T (P*tS)^T, 8 MFMAs per key chunk
+      static_for<0, 4>([&](auto icc) {
+        constexpr int cc = decltype(icc)::value;
+        static_for<0, C::kBlocksD>([&](auto ib) {
+          constexpr int b = decltype(ib)::value;
+          acc_o[b] = mfma(vf[b], pr.pf[cc], acc_o[b]);
+          work(std::integral_constant<int, 2 * C::kBlocksD * cc + 2 * b>{});
+          fence();
+          acc_t[b] = mfma(vf[b], pr.ptf[cc], acc_t[b]);
+          if constexpr (cc + 1 < 4) vf[b] = load_v(stage, cc + 1, b, 0);
+          work(std::integral_constant<int, 2 * C::kBlocksD * cc + 2 * b + 1>{});
+          fence();
+        });
+      });
+      return;
+    }
     static_for<0, 4>([&](auto icc) {
       constexpr int cc = decltype(icc)::value;
       static_for<0, C::kBlocksD>([&](auto ib) {
@@ -419,9 +444,9 @@ void attn_jvp_bf16_kernel(Params p) {
       });
     });
   };
-  constexpr int kUnitsA = 6 * C::kChunksD;   // logit MFMAs of one tile
+  constexpr int kUnitsA = kUPC * C::kChunksD;  // logit MFMAs of one tile
   constexpr int kPreSlots = 2;               // softmax slots run before the first logit MFMA
-  constexpr int kUnitsB = 12 * C::kBlocksD;  // MFMAs of products(), numbered 0 .. kUnitsB - 1
+  constexpr int kUnitsB = (kFrozen ? 8 : 12) * C::kBlocksD;  // MFMAs of products(), 0 .. kUnitsB - 1
 
   const int nt = (Lk + kBc - 1) / kBc;
   const bool ragged = (Lk % kBc) != 0;
@@ -438,7 +463,7 @@ void attn_jvp_bf16_kernel(Params p) {
     static_for<0, C::kChunksD>([&](auto ic) {
       bf16x8 k[4];
       load_k(smem, decltype(ic)::value, k);
-      static_for<0, 6>([&](auto iu) { logit_mfma(iu, ic, k, sn, tsn); });
+      static_for<0, kUPC>([&](auto iu) { logit_mfma(iu, ic, k, sn, tsn); });
     });
     fence();
     if (nt == 1 && ragged) mask_tail<2>(sn, Lk, hh);
@@ -471,10 +496,10 @@ void attn_jvp_bf16_kernel(Params p) {
       if constexpr (c + 1 < C::kChunksD) load_k(kstage, c + 1, kf[(c + 1) & 1]);
       // the chunk-0 V fragments of the products are read under the last chunk
       if constexpr (c + 1 == C::kChunksD) load_v0(vstage, vf, tvf);
-      static_for<0, 6>([&](auto iu) {
+      static_for<0, kUPC>([&](auto iu) {
         constexpr int u = decltype(iu)::value;
         logit_mfma(iu, ic, kf[c & 1], sn, tsn);
-        constexpr int g = 6 * c + u;
+        constexpr int g = kUPC * c + u;
         pipeline_slot(IC<g + kPreSlots>{}, IC<kUnitsA>{}, IC<32>{}, IC<4>{}, elem);
         // the tile copies of this iteration (K|tK of tile j + 2, V|tV of tile
         // j + 1) are spread over the phase-A units instead of one burst at the
@@ -586,7 +611,7 @@ void attn_jvp_bf16_kernel(Params p) {
   }
 }
 
-template <int D>
+template <int D, bool kFrozen>
 hipError_t launch(const Problem& pr, hipStream_t stream) {
   Params p;
   p.q = pr.q; p.k = pr.k; p.v = pr.v; p.tq = pr.tq; p.tk = pr.tk; p.tv = pr.tv;
@@ -594,14 +619,16 @@ hipError_t launch(const Problem& pr, hipStream_t stream) {
   p.Lq = pr.Lq; p.Lk = pr.Lk; p.kv_rows = pr.kv_rows; p.scale = pr.scale;
   p.n_qtiles = (pr.Lq + kBlockRows - 1) / kBlockRows;
   p.n_blocks = pr.B * pr.H * p.n_qtiles;
-  hipLaunchKernelGGL(attn_jvp_bf16_kernel<D>, dim3(p.n_blocks), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_jvp_bf16_kernel<D, kFrozen>), dim3(p.n_blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bf16(const Problem& p, hipStream_t stream) {
-  return p.d == 128 ? launch<128>(p, stream) : launch<64>(p, stream);
+  if (p.tk == nullptr)  // frozen context: tK = tV = 0
+    return p.d == 128 ? launch<128, true>(p, stream) : launch<64, true>(p, stream);
+  return p.d == 128 ? launch<128, false>(p, stream) : launch<64, false>(p, stream);
 }
 
 }  // namespace attnjvp

@@ -101,8 +101,10 @@ void attn_jvp_fp32_kernel(Params p) {
   const auto rq = make_rsrc((const char*)p.q + qhead, qbytes);
   const auto rtq = make_rsrc((const char*)p.tq + qhead, qbytes);
   const __amdgpu_buffer_rsrc_t rkv[4] = {
-      make_rsrc((const char*)p.k + khead, kbytes), make_rsrc((const char*)p.tk + khead, kbytes),
-      make_rsrc((const char*)p.v + khead, kbytes), make_rsrc((const char*)p.tv + khead, kbytes)};
+      make_rsrc((const char*)p.k + khead, kbytes),
+      p.tk ? make_rsrc((const char*)p.tk + khead, kbytes) : make_rsrc(p.k, 0),  // NULL: an empty range reads zeros
+      make_rsrc((const char*)p.v + khead, kbytes),
+      p.tv ? make_rsrc((const char*)p.tv + khead, kbytes) : make_rsrc(p.v, 0)};
 
   // Lane (n, hh) keeps dims hh*D/2 .. hh*D/2 + D/2 - 1 of its query's Q and tQ.
   const int qrow = qt * kBlockRows + wv * kWaveRows + n;

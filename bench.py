@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix/vector, vendor figure
 METRIC = "attention-JVP TFLOP/s (12*B*H*Lq*Lk*d) + % bf16 MFMA peak, 1 MI355X"
+METRIC_FROZEN = "attention-JVP executed TFLOP/s, frozen context (8*B*H*Lq*Lk*d) + % bf16 MFMA peak, 1 MI355X"
 KERNEL_SOURCES = ["attention_forward_mode_attn_amd/csrc/kernel_bf16.hip",
                   "attention_forward_mode_attn_amd/csrc/kernel_fp32.hip",
                   "attention_forward_mode_attn_amd/csrc/device_common.h"]
@@ -112,6 +113,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--cpu-rows-per-head", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--frozen-context", action="store_true",
+                    help="pass tk = tv = NULL (workloads whose key tangents are zero); "
+                         "value is then executed TFLOP/s at 8 flops per logit and head dim")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -127,6 +131,12 @@ def main():
 
     from workloads.device import device_inputs
 
+    w = WORKLOADS[args.workload]
+    if args.frozen_context and (w.std.get("tk", 1.0) != 0.0 or w.std.get("tv", 1.0) != 0.0):
+        print(f"bench.py: --frozen-context needs a workload with tK = tV = 0 ({w.name} has key tangents)",
+              file=sys.stderr)
+        sys.exit(2)
+
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -140,7 +150,6 @@ def main():
         print(json.dumps({"copy_bytes": n, "launches": args.warmup + args.steps}))
         return
 
-    w = WORKLOADS[args.workload]
     print(f"bench: {w.name} B{w.B} H{w.H} Lq{w.Lq} Lk{w.Lk} d{w.d} {w.dtype}: generating inputs",
           file=sys.stderr, flush=True)
     x = device_inputs(w)
@@ -149,8 +158,10 @@ def main():
     lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    tk, tv = (None, None) if args.frozen_context else (x["tk"], x["tv"])
+
     def step():
-        A.fwd(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], scale=w.scale, out=(o, to, lse), stream=stream)
+        A.fwd(x["q"], x["k"], x["v"], x["tq"], tk, tv, scale=w.scale, out=(o, to, lse), stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -173,7 +184,8 @@ def main():
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
     ms_per_step = total_ms / args.steps
 
-    flops = w.flops
+    # executed work: the frozen-context path skips the tK Q^T and tV P^T products
+    flops = w.flops * (8.0 / 12.0 if args.frozen_context else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
@@ -183,8 +195,9 @@ def main():
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": measured_traffic(w.name),
-        "kernel": "attn_jvp_bf16_kernel<128>" if w.dtype == "bf16" else f"attn_jvp_fp32_kernel<{w.d}>",
+        "traffic": None if args.frozen_context else measured_traffic(w.name),
+        "kernel": (f"attn_jvp_bf16_kernel<{w.d}, {str(args.frozen_context).lower()}>" if w.dtype == "bf16"
+                   else f"attn_jvp_fp32_kernel<{w.d}>"),
         "avg_launch_ms": round(avg_launch_ms, 4),
         "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4),
         "min_launch_ms": round(launch_ms[0], 4),
@@ -192,7 +205,7 @@ def main():
         "algorithmic_bytes_per_launch": w.algorithmic_bytes,
     }
     out = {
-        "metric": METRIC,
+        "metric": METRIC_FROZEN if args.frozen_context else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -205,7 +218,9 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "d": w.d,
-                   "scale": w.scale, "parallelism": "single GPU"},
+                   "scale": w.scale, "parallelism": "single GPU",
+                   "path": "frozen context (tk = tv = NULL; 8 executed flops per logit and head dim)"
+                   if args.frozen_context else "full JVP (12 flops per logit and head dim)"},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "wall_s_timed_region": round(wall, 3),
         "roofline": roofline,

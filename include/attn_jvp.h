@@ -63,6 +63,11 @@ typedef enum {
  *   q, tq   [B, H, Lq, d]  queries and their tangent                (device, read only)
  *   k, tk   [B, H, Lk, d]  keys and their tangent                   (device, read only)
  *   v, tv   [B, H, Lk, d]  values and their tangent                 (device, read only)
+ *           tk and tv may both be NULL: a frozen context, tK = tV = 0 (the
+ *           text cross-attention of the pages: papernotes.org notes, "Key
+ *           designs" item 1).  The bf16 path then skips the tK and tV
+ *           products and copies (8 instead of 12 flops per logit and head
+ *           dim); the result equals passing zero-filled tk, tv.
  *   o, to   [B, H, Lq, d]  outputs: attention output and its tangent (device, written)
  *   lse     [B, H, Lq]     float32 row log-sum-exp of scale*QK^T     (device, written)
  *   B, H, Lq, Lk, d        sizes; d in {64, 128}
@@ -84,7 +89,8 @@ typedef enum {
  * reproducible.
  *
  * Errors: all argument checks run on the host before any HIP call, and a
- * failed check launches nothing.  B*H*Lq == 0 is a no-op returning ATTN_JVP_OK
+ * failed check launches nothing.  Exactly one of tk, tv NULL is
+ * ATTN_JVP_EINVAL.  B*H*Lq == 0 is a no-op returning ATTN_JVP_OK
  * (pointers are then not inspected).  Limits: Lq*d and Lk*d below 2^29
  * elements per head, B*H*ceil(Lq/128) below 2^31.  The library never aborts.
  * Non-finite input values propagate into the outputs; they are not detected.

@@ -101,6 +101,21 @@ def test_fwd_rejects_bad_tensors_before_launch(lib):
         A.fwd(*(torch.zeros(1, 1, 4, 64, dtype=torch.float16),) * 6)
 
 
+def test_null_key_tangents_must_come_in_pairs(lib):
+    assert call(ptrs=[FAKE] * 4 + [0] + [FAKE] * 3) == A.ATTN_JVP_EINVAL
+    assert "both be NULL" in A.attn_jvp_last_error()
+    assert call(ptrs=[FAKE] * 5 + [0] + [FAKE] * 2) == A.ATTN_JVP_EINVAL
+
+
+def test_frozen_context_passes_host_checks(lib):
+    """tk = tv = NULL is a valid call: with no GPU it reaches the launch."""
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this checks the no-device path only")
+    assert call(ptrs=[FAKE] * 4 + [0, 0] + [FAKE] * 2) == A.ATTN_JVP_ELAUNCH
+
+
 def test_no_device_returns_launch_error(lib):
     """With no GPU present a well-formed call reports ELAUNCH instead of aborting."""
     import torch
