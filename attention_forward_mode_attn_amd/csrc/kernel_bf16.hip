@@ -26,9 +26,14 @@
 //    row running sums l = sum p and a = sum p*tS, and the epilogue
 //      O = acc_o / l,  tO = (acc_t - (a / l) acc_o) / l,  lse = (m + log2 l) ln 2;
 //  * software pipeline: iteration j computes the softmax of tile j under the
-//    logit MFMAs of tile j + 1 (phase A), then the product MFMAs of tile j under
-//    the max reduction of tile j + 1 (phase B), written as fenced units of one
-//    MFMA plus a slice of VALU work so that the two execute together.
+//    logit MFMAs of tile j + 1 (phase A), then the product MFMAs of tile j
+//    while the logits of tile j + 1 leave their accumulators, already scaled
+//    and shifted for the exponentials (phase B); written as fenced units of
+//    one MFMA plus a slice of VALU work, the VALU steps of each item staged
+//    one unit apart so that no unit waits on its own results;
+//  * variants: a frozen context (tK = tV = 0) skips the tK and tV products
+//    and copies; a key shard (kv_rows > Lk) is the same pass on part of the
+//    keys, with the tangent of lse as an extra output for an exact merge.
 #include <type_traits>
 
 #include "device_common.h"
