@@ -270,6 +270,11 @@ void attn_jvp_bf16_kernel(Params p) {
       kf[3] = *reinterpret_cast<const bf16x8*>(stage + C::kTile + 32 * C::kRow + u);
     }
   };
+  // One of those four fragments: x = 2 * (tK ? 1 : 0) + key block.
+  auto load_k1 = [&](const char* stage, int c, int x, bf16x8 (&kf)[4]) {
+    const uint32_t u = krow + (((2 * c + hh) ^ ksw) << 4);
+    kf[x] = *reinterpret_cast<const bf16x8*>(stage + (x & 2 ? C::kTile : 0) + (x & 1 ? 32 * C::kRow : 0) + u);
+  };
   // V fragment via ds_read_b64_tr_b16: in 16-lane group G = lane / 16 (half
   // hh = G / 2, dims 16(G & 1) .. +15 of the 32-dim block), source lane s reads
   // 4 dims starting at 4(s & 3) of key 4hh + (s >> 2) (+ 16cc, + 8 for the
@@ -496,21 +501,27 @@ void attn_jvp_bf16_kernel(Params p) {
     // while the first K fragments are in flight: the first softmax slots
     static_for<0, kPreSlots>([&](auto ig) { pipeline_slot(ig, IC<kUnitsA>{}, IC<32>{}, IC<4>{}, elem); });
     fence();
+    constexpr int kKFrags = kFrozen ? 2 : 4;  // K fragments per chunk
     static_for<0, C::kChunksD>([&](auto ic) {
       constexpr int c = decltype(ic)::value;
-      if constexpr (c + 1 < C::kChunksD) load_k(kstage, c + 1, kf[(c + 1) & 1]);
-      // the chunk-0 V fragments of the products are read under the last chunk
-      if constexpr (c + 1 == C::kChunksD) load_v0(vstage, vf, tvf);
       static_for<0, kUPC>([&](auto iu) {
         constexpr int u = decltype(iu)::value;
         logit_mfma(iu, ic, kf[c & 1], sn, tsn);
         constexpr int g = kUPC * c + u;
-        pipeline_slot(IC<g + kPreSlots>{}, IC<kUnitsA>{}, IC<32>{}, IC<4>{}, elem);
-        // the tile copies of this iteration (K|tK of tile j + 2, V|tV of tile
-        // j + 1) are spread over the phase-A units instead of one burst at the
-        // top, where they would compete with the first K fragment reads
+        // Each unit: the MFMA, then the tile copies of this iteration (K|tK of
+        // tile j + 2, V|tV of tile j + 1) spread over the phase-A units, then
+        // one K fragment of the next chunk (or, in the last chunk, the
+        // chunk-0 V fragments of one dim block for the products), then its
+        // softmax slot.  Issuing the copies first and reading the fragments
+        // one per unit measured faster than bursts at the chunk start.
         static_for<(g * kDmaPerIter + kUnitsA - 1) / kUnitsA, ((g + 1) * kDmaPerIter + kUnitsA - 1) / kUnitsA>(
             [&](auto iq) { issue_q(j, iq); });
+        if constexpr (c + 1 < C::kChunksD && u < kKFrags) load_k1(kstage, c + 1, u, kf[(c + 1) & 1]);
+        if constexpr (c + 1 == C::kChunksD && u < C::kBlocksD) {
+          vf[u] = load_v(vstage, 0, u, 0);
+          if constexpr (!kFrozen) tvf[u] = load_v(vstage, 0, u, 1);
+        }
+        pipeline_slot(IC<g + kPreSlots>{}, IC<kUnitsA>{}, IC<32>{}, IC<4>{}, elem);
         fence();
       });
     });
