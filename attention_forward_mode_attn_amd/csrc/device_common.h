@@ -29,9 +29,13 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Rescale threshold (log2 units): the running max used for exponentiation is
 // only moved when a row's max grows by more than this, so exp2 arguments stay
-// <= kRescaleSlack and p <= 2^8.  Softmax is shift invariant, so the result is
-// the same up to rounding.
-constexpr float kRescaleSlack = 8.0f;
+// <= kRescaleSlack and p <= 2^32.  Softmax is shift invariant, so the result is
+// the same up to rounding (relative rounding does not depend on magnitude).
+// Headroom: with Lk < 2^23 the sums stay below 2^55 * max|v|, far from fp32
+// overflow for any input below 2^73 in magnitude; weights more than 2^-94 below
+// the row max flush to zero.  A large slack keeps peaky softmaxes (logit std
+// ~8) from leaving the hot loop to rescale on most tiles.
+constexpr float kRescaleSlack = 32.0f;
 
 // Buffer resource over [base, base + bytes): loads past the end return 0 and
 // stores past the end are dropped by the hardware range check.
