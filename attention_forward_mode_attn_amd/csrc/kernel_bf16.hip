@@ -601,22 +601,53 @@ void attn_jvp_bf16_kernel(Params p) {
   const float inv = 1.0f / l, mu = a * inv;
   const auto ro = make_rsrc((const char*)p.o + qhead, qbytes);
   const auto rto = make_rsrc((const char*)p.to + qhead, qbytes);
+  // Accumulator group g (registers 4g..4g+3) of a lane holds head dims
+  // 8g + 4hh .. +3 of its query.  Groups g, g + 1 (g even) are paired across the
+  // half-waves with v_permlane32_swap so that each lane holds 8 consecutive
+  // dims: half 0 dims 8g .. 8g + 7, half 1 dims 8(g + 1) .. +7, one 16-byte
+  // store each.  Every value is packed into its own registers before the
+  // first store: reusing a store's data registers right after it makes the
+  // next write wait until the queued store has read them.
+  u32x4 ost[C::kBlocksD][2], tst[C::kBlocksD][2];
+  auto pair = [](u32x2 x, u32x2 y) {  // x: group g, y: group g + 1 of this lane
+    const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
+    return u32x4{s0[0], s1[0], s0[1], s1[1]};
+  };
 #pragma unroll
   for (int b = 0; b < C::kBlocksD; ++b) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float ov[4], tv4[4];
+    for (int gp = 0; gp < 2; ++gp) {
+      u32x2 op[2], tp[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = acc_o[b][4 * g + i];
-        ov[i] = x * inv;
-        tv4[i] = (acc_t[b][4 * g + i] - mu * x) * inv;
+      for (int h = 0; h < 2; ++h) {
+        const int g = 2 * gp + h;
+        float ov[4], tv4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = acc_o[b][4 * g + i];
+          ov[i] = x * inv;
+          tv4[i] = (acc_t[b][4 * g + i] - mu * x) * inv;
+        }
+        op[h] = u32x2{pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3])};
+        tp[h] = u32x2{pack_bf16(tv4[0], tv4[1]), pack_bf16(tv4[2], tv4[3])};
       }
-      const uint32_t off = ((uint32_t)qrow * D + 32 * b + 8 * g + 4 * hh) * 2;
-      buf_store8(ro, off, u32x2{pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3])});
-      buf_store8(rto, off, u32x2{pack_bf16(tv4[0], tv4[1]), pack_bf16(tv4[2], tv4[3])});
+      ost[b][gp] = pair(op[0], op[1]);
+      tst[b][gp] = pair(tp[0], tp[1]);
     }
   }
+  fence();
+  // one address register for all stores; the (b, gp) part rides in the scalar
+  // offset (read at issue, so reusing it does not wait on earlier stores).
+  // Rows past Lq have obase past the end of the range: their stores drop.
+  const uint32_t obase = ((uint32_t)qrow * D + 8 * hh) * 2;
+#pragma unroll
+  for (int b = 0; b < C::kBlocksD; ++b)
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) {
+      __builtin_amdgcn_raw_buffer_store_b128(ost[b][gp], ro, obase, (32 * b + 16 * gp) * 2, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(tst[b][gp], rto, obase, (32 * b + 16 * gp) * 2, 0);
+    }
   if (hh == 0) {
     const auto rl = make_rsrc((const char*)p.lse + (size_t)bh * Lq * 4, (uint32_t)Lq * 4);
     buf_store4(rl, (uint32_t)qrow * 4, (st.m + __builtin_amdgcn_logf(l)) * kLn2);
