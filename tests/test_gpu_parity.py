@@ -168,3 +168,34 @@ def test_tangent_along_values_gives_output(A):
     print(f"  |tO - O| / max|O| = {d:.3e}", flush=True)
     assert d <= 2e-2
     assert np.isfinite(d)
+
+
+RAMPS = [
+    # (B, H, Lq, Lk, d, dtype, key_ramp): key row j scaled by 1 + ramp * j, so
+    # the row max rises by more than the lazy base's slack on most tiles and the
+    # hot loop leaves to rescale again and again (jumps up to ~100 log2 units)
+    (1, 2, 130, 1000, 128, "bf16", 0.05),
+    (1, 1, 200, 700, 64, "bf16", 0.08),
+    (1, 1, 129, 300, 64, "fp32", 0.1),
+]
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,d,dtype,ramp", RAMPS)
+def test_rising_logits_rescale_path(A, B, H, Lq, Lk, d, dtype, ramp):
+    w = custom_workload(B, H, Lq, Lk, d, dtype, seed_id=5000 + Lk, key_ramp=ramp)
+    print(f"case key ramp {ramp} B{B} H{H} Lq{Lq} Lk{Lk} d{d} {dtype}", flush=True)
+    _, o, to, lse = run(A, w)
+    check(w, compare(w, o, to, lse))
+
+
+def test_rising_logits_frozen_and_split(A):
+    std = {"q": 1.0, "k": 1.0, "v": 1.0, "tq": 1.0, "tk": 0.0, "tv": 0.0}
+    w = custom_workload(1, 2, 130, 1000, 128, "bf16", seed_id=5100, std=std, key_ramp=0.05)
+    print("case key ramp, frozen, 4 shards", flush=True)
+    x = device_inputs(w)
+    o, to, lse, tlse = A.fwd_split(x["q"], x["k"], x["v"], x["tq"], None, None, 4, scale=w.scale)
+    torch.cuda.synchronize()
+    res = compare(w, o, to, lse, tlse=tlse)
+    print(f"  tlse {res['tlse']:.3e}", flush=True)
+    check(w, res)
+    assert res["tlse"] <= TOL[w.dtype]

@@ -76,3 +76,16 @@ def test_oracle_regression_fixture():
         assert np.allclose(O, e["O"], rtol=0, atol=1e-13)
         assert np.allclose(tO, e["tO"], rtol=0, atol=1e-13)
         assert np.allclose(lse, e["lse"], rtol=0, atol=1e-13)
+
+
+def test_key_ramp_scales_key_rows_only():
+    import numpy as np
+
+    from workloads import custom_workload, head_array
+
+    flat = custom_workload(1, 1, 8, 40, 64, "fp32", seed_id=77)
+    ramp = custom_workload(1, 1, 8, 40, 64, "fp32", seed_id=77, key_ramp=0.25)
+    k0, k1 = head_array(flat, "k", 0, 0), head_array(ramp, "k", 0, 0)
+    assert np.array_equal(k1, k0 * (1 + 0.25 * np.arange(40, dtype=np.float32))[:, None])
+    for t in ("q", "v", "tq", "tk", "tv"):
+        assert np.array_equal(head_array(flat, t, 0, 0), head_array(ramp, t, 0, 0))

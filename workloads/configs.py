@@ -30,6 +30,9 @@ class Workload:
     std: dict = field(default_factory=dict)  # per-tensor standard deviation
     # When set, tq of head h is additionally scaled by 10**U(-2, 2) drawn per head.
     per_head_tq_scale: bool = False
+    # Key row j is additionally scaled by 1 + key_ramp * j (0: no ramp): logits
+    # that grow along the keys, so the row max keeps rising tile after tile.
+    key_ramp: float = 0.0
     description: str = ""
 
     @property
@@ -96,6 +99,7 @@ WORKLOADS = {
 }
 
 
-def custom_workload(B, H, Lq, Lk, d, dtype, seed_id=1000, std=None, name="custom") -> Workload:
+def custom_workload(B, H, Lq, Lk, d, dtype, seed_id=1000, std=None, name="custom", key_ramp=0.0) -> Workload:
     """An ad-hoc shape (ragged tails, edge cases) with the default N(0,1) inputs."""
-    return Workload(name, seed_id, B=B, H=H, Lq=Lq, Lk=Lk, d=d, dtype=dtype, std=std or _std())
+    return Workload(name, seed_id, B=B, H=H, Lq=Lq, Lk=Lk, d=d, dtype=dtype, std=std or _std(),
+                    key_ramp=key_ramp)

@@ -53,6 +53,8 @@ def _raw_head(w: Workload, tensor: str, b: int, h: int) -> np.ndarray:
     x = _rng(w.seed_id, ti, b, h).standard_normal((L, w.d), dtype=np.float32)
     if std != 1.0:
         x *= np.float32(std)
+    if tensor == "k" and w.key_ramp:
+        x *= (np.float32(1.0) + np.float32(w.key_ramp) * np.arange(L, dtype=np.float32))[:, None]
     return x
 
 
