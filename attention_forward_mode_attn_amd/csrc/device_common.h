@@ -56,6 +56,25 @@ __device__ inline void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, float 
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds):
+// lane l of the wave writes LDS bytes lds_addr + 16 l .. + 15.
+// It is issued with inline asm rather than the builtin on purpose: the
+// compiler treats a builtin LDS DMA as a store that may alias every LDS read
+// that follows, and waits for it (vmcnt(0)) before the next read even though
+// the two stages never overlap.  Here the pipeline orders the copies itself:
+// each stage is refilled only after a barrier that follows its last read, and
+// read only after an explicit vmcnt(0) and a barrier.  The instruction has no
+// register outputs; its LDS destination (a wave-uniform LDS byte address) is
+// passed in M0.
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(lds_addr) : "memory");
+}
+
+// LDS byte address of a __shared__ object.
+__device__ inline uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
 // Renumber them so that XCD x owns one contiguous range of logical ids: the
 // query tiles of one head then run on the same XCD and share K/V in its L2.

@@ -107,23 +107,6 @@ __device__ inline uint32_t tile_load_voff(int blk, int lane, bool vswz) {
   return (uint32_t)(r * C::kRow + u * 16);
 }
 
-// The copy is issued with inline asm rather than the builtin on purpose: the
-// compiler treats a builtin LDS DMA as a store that may alias every LDS read
-// that follows, and waits for it (vmcnt(0)) before the next read even though
-// the two stages never overlap.  Here the pipeline orders the copies itself:
-// each stage is refilled only after a barrier that follows its last read, and
-// read only after an explicit vmcnt(0) and a barrier.  The instruction has no
-// register outputs; its LDS destination (a wave-uniform LDS byte address) is
-// passed in M0.
-__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(lds_addr) : "memory");
-}
-
-// LDS byte address of a __shared__ object.
-__device__ inline uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
-}
-
 // LDS read helpers.
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 __device__ inline i16x4 lds_tr16(const char* p) {

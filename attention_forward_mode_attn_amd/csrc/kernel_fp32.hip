@@ -36,10 +36,9 @@ template <int D>
 struct Cfg {
   static constexpr int kTile = kBcF * D * 4;           // bytes of one tile, [key][dim]
   static constexpr int kStage = 4 * kTile;             // K, tK, V, tV
-  static constexpr int kUnits = kBcF * D / 4;          // 16-byte units in a tile
-  static constexpr int kPerThread = kUnits / kThreads;
+  static constexpr int kLoadsPerWave = kTile / 1024 / kWaves;  // 1 KB copies per tensor per tile
   static constexpr int kBlocksD = D / 32;
-  static_assert(kUnits % kThreads == 0, "tile split");
+  static_assert(kTile % (1024 * kWaves) == 0, "tile split");
 };
 
 // K/tK rows are XOR-swizzled by 16-byte unit so that the 16 lanes that a
@@ -55,40 +54,21 @@ __device__ inline f32x16 mfma(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// Tiles go global -> LDS by buffer_load ... lds: the lane that fills LDS slot
+// 16 s of a tile (row r = s / (D/4), physical unit pu) fetches the 16 bytes of
+// logical unit pu ^ (r & 15) for K/tK (the swizzle of k_off), pu for V/tV.
+// Rows past Lk read as zero (buffer range check).
 template <int D>
-struct Staging {
-  u32x4 x[4][Cfg<D>::kPerThread];
-};
-
-template <int D>
-__device__ inline void issue_tile_loads(Staging<D>& sg, const __amdgpu_buffer_rsrc_t (&r)[4], int key0, int t) {
-#pragma unroll
-  for (int tn = 0; tn < 4; ++tn)
-#pragma unroll
-    for (int i = 0; i < Cfg<D>::kPerThread; ++i) {
-      const int e = t + kThreads * i;
-      sg.x[tn][i] = buf_load16(r[tn], ((uint32_t)key0 * D + e * 4) * 4);
-    }
-}
-
-template <int D>
-__device__ inline void store_tile(const Staging<D>& sg, char* stage, int t) {
-#pragma unroll
-  for (int i = 0; i < Cfg<D>::kPerThread; ++i) {
-    const int e = t + kThreads * i;
-    const int row = e / (D / 4), u = e % (D / 4);
-    *reinterpret_cast<u32x4*>(stage + k_off<D>(row, u)) = sg.x[0][i];
-    *reinterpret_cast<u32x4*>(stage + Cfg<D>::kTile + k_off<D>(row, u)) = sg.x[1][i];
-    *reinterpret_cast<u32x4*>(stage + 2 * Cfg<D>::kTile + e * 16) = sg.x[2][i];
-    *reinterpret_cast<u32x4*>(stage + 3 * Cfg<D>::kTile + e * 16) = sg.x[3][i];
-  }
+__device__ inline uint32_t tile_voff(int slice, int lane, bool kswz) {
+  const int slot = slice * 64 + lane, r = slot / (D / 4), pu = slot % (D / 4);
+  return (uint32_t)(r * D + 4 * (kswz ? (pu ^ (r & 15)) : pu)) * 4;
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_jvp_fp32_kernel(Params p) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kStage];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStage];
 
   const int t = threadIdx.x;
   const int lane = t & 63, wv = t >> 6, n = lane & 31, hh = lane >> 5;
@@ -160,10 +140,26 @@ void attn_jvp_fp32_kernel(Params p) {
     }
   };
 
+  // Tile j lives in LDS stage j & 1; tile j + 1 is copied while tile j is used
+  // (its stage was last read before the previous barrier).
+  uint32_t voff_k[C::kLoadsPerWave], voff_v[C::kLoadsPerWave];
+#pragma unroll
+  for (int i = 0; i < C::kLoadsPerWave; ++i) {
+    voff_k[i] = tile_voff<D>(wv * C::kLoadsPerWave + i, lane, true);
+    voff_v[i] = tile_voff<D>(wv * C::kLoadsPerWave + i, lane, false);
+  }
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  auto issue = [&](int j) {
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+      for (int i = 0; i < C::kLoadsPerWave; ++i)
+        lds_dma16(rkv[tn], smem_lds + (j & 1) * C::kStage + tn * C::kTile + (wv * C::kLoadsPerWave + i) * 1024,
+                  (tn < 2 ? voff_k[i] : voff_v[i]) + (uint32_t)j * C::kTile);
+  };
   const int nt = (Lk + kBcF - 1) / kBcF;
-  Staging<D> sg;
-  issue_tile_loads<D>(sg, rkv, 0, t);
-  store_tile<D>(sg, smem, t);
+  issue(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   int j = 0;
   f32x16 s, ts;
@@ -174,7 +170,7 @@ void attn_jvp_fp32_kernel(Params p) {
     bool rescale = false;
     for (; j < nt; ++j) {
       const char* cur = smem + (j & 1) * C::kStage;
-      if (j + 1 < nt) issue_tile_loads<D>(sg, rkv, (j + 1) * kBcF, t);
+      if (j + 1 < nt) issue(j + 1);
 
       s = f32x16{};
       ts = f32x16{};
@@ -207,7 +203,7 @@ void attn_jvp_fp32_kernel(Params p) {
       float pv[16], ptv[16];
       probabilities(s, ts, pv, ptv);
       accumulate(cur, pv, ptv);
-      if (j + 1 < nt) store_tile<D>(sg, smem + ((j + 1) & 1) * C::kStage, t);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile j + 1 of this wave landed
       __syncthreads();
     }
     if (!rescale) break;
@@ -220,7 +216,7 @@ void attn_jvp_fp32_kernel(Params p) {
     float pv[16], ptv[16];
     probabilities(s, ts, pv, ptv);
     accumulate(smem + (j & 1) * C::kStage, pv, ptv);
-    if (j + 1 < nt) store_tile<D>(sg, smem + ((j + 1) & 1) * C::kStage, t);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     ++j;
   }
@@ -229,22 +225,30 @@ void attn_jvp_fp32_kernel(Params p) {
   const float inv = 1.0f / l, mu = a * inv;
   const auto ro = make_rsrc((const char*)p.o + qhead, qbytes);
   const auto rto = make_rsrc((const char*)p.to + qhead, qbytes);
+  // All values first (each in its own registers), then the stores from one
+  // address register: reusing a store's registers right after issuing it makes
+  // the next write wait until the queued store has read them.  Group g of a
+  // lane holds dims 8g + 4hh .. +3 of its query (16 bytes).
+  u32x4 ov[C::kBlocksD][4], tv4[C::kBlocksD][4];
 #pragma unroll
-  for (int b = 0; b < C::kBlocksD; ++b) {
+  for (int b = 0; b < C::kBlocksD; ++b)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x4 ov, tv4;
+    for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float x = acc_o[b][4 * g + i];
-        ov[i] = __float_as_uint(x * inv);
-        tv4[i] = __float_as_uint((acc_t[b][4 * g + i] - mu * x) * inv);
+        ov[b][g][i] = __float_as_uint(x * inv);
+        tv4[b][g][i] = __float_as_uint((acc_t[b][4 * g + i] - mu * x) * inv);
       }
-      const uint32_t off = ((uint32_t)qrow * D + 32 * b + 8 * g + 4 * hh) * 4;
-      buf_store16(ro, off, ov);
-      buf_store16(rto, off, tv4);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint32_t obase = ((uint32_t)qrow * D + 4 * hh) * 4;  // rows past Lq: out of range, dropped
+#pragma unroll
+  for (int b = 0; b < C::kBlocksD; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __builtin_amdgcn_raw_buffer_store_b128(ov[b][g], ro, obase, (32 * b + 8 * g) * 4, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(tv4[b][g], rto, obase, (32 * b + 8 * g) * 4, 0);
     }
-  }
   if (hh == 0) {
     const auto rl = make_rsrc((const char*)p.lse + (size_t)bh * Lq * 4, (uint32_t)Lq * 4);
     buf_store4(rl, (uint32_t)qrow * 4, (st.m + __builtin_amdgcn_logf(l)) * kLn2);
