@@ -29,9 +29,11 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix/vector, vendor figure
 METRIC = "attention-JVP TFLOP/s (12*B*H*Lq*Lk*d) + % bf16 MFMA peak, 1 MI355X"
 METRIC_FROZEN = "attention-JVP executed TFLOP/s, frozen context (8*B*H*Lq*Lk*d) + % bf16 MFMA peak, 1 MI355X"
+# The sources of the bf16 kernel whose HBM traffic profiles/ records: a change
+# to any of them makes the recorded traffic stale (reported as null).
 KERNEL_SOURCES = ["attention_forward_mode_attn_amd/csrc/kernel_bf16.hip",
-                  "attention_forward_mode_attn_amd/csrc/kernel_fp32.hip",
-                  "attention_forward_mode_attn_amd/csrc/device_common.h"]
+                  "attention_forward_mode_attn_amd/csrc/device_common.h",
+                  "attention_forward_mode_attn_amd/csrc/launch.h"]
 
 
 def kernel_source_hash() -> str:
