@@ -46,12 +46,6 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
-__device__ inline void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
-}
-__device__ inline void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
-}
 __device__ inline void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }

@@ -144,11 +144,12 @@ __device__ inline void fence() { __builtin_amdgcn_sched_barrier(0); }
 __device__ inline void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ inline void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
 
+template <int I>
+using IC = std::integral_constant<int, I>;
+
 // Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E).  Every
 // register-array index in the pipelined loop is a constant, so the arrays stay
 // in registers (a runtime index would send them to memory).
-template <int I>
-using IC = std::integral_constant<int, I>;
 template <int B, int E, typename F>
 __device__ inline void static_for(F&& f) {
   if constexpr (B < E) {
