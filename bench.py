@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, vendor figure
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix/vector, vendor figure
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, vendor figure
 METRIC = "attention-JVP TFLOP/s (12*B*H*Lq*Lk*d) + % bf16 MFMA peak, 1 MI355X"
 METRIC_FROZEN = "attention-JVP executed TFLOP/s, frozen context (8*B*H*Lq*Lk*d) + % bf16 MFMA peak, 1 MI355X"
 # The sources of the bf16 kernel whose HBM traffic profiles/ records: a change
@@ -115,11 +116,17 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--cpu-rows-per-head", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--split", type=int, default=0,
+                    help="time the key-sharded path: N attn_jvp_fwd_part passes plus attn_jvp_merge; "
+                         "the roofline object then covers the merge launch (HBM bound)")
     ap.add_argument("--frozen-context", action="store_true",
                     help="pass tk = tv = NULL (workloads whose key tangents are zero); "
                          "value is then executed TFLOP/s at 8 flops per logit and head dim")
     args = ap.parse_args()
 
+    if args.split and not 1 <= args.split <= 16:
+        print("bench.py: --split must be in 1 .. 16 (ATTN_JVP_MAX_MERGE_PARTS)", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
               "(the attention JVP shards by (batch, head) with no exchange: run one process per GPU)",
@@ -161,9 +168,26 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     tk, tv = (None, None) if args.frozen_context else (x["tk"], x["tv"])
+    if args.split:
+        bounds = A.shard_bounds(w.Lk, args.split)
+        parts = [(torch.empty_like(o), torch.empty_like(o), torch.empty_like(lse), torch.empty_like(lse))
+                 for _ in bounds]
+        tlse = torch.empty_like(lse)
+        merge_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for _ in range(args.warmup + args.steps)]
+        n_step = [0]
 
     def step():
-        A.fwd(x["q"], x["k"], x["v"], x["tq"], tk, tv, scale=w.scale, out=(o, to, lse), stream=stream)
+        if not args.split:
+            A.fwd(x["q"], x["k"], x["v"], x["tq"], tk, tv, scale=w.scale, out=(o, to, lse), stream=stream)
+            return
+        for (k0, k1), part in zip(bounds, parts):
+            A.fwd_part(x["q"], x["k"], x["v"], x["tq"], tk, tv, k0, k1, scale=w.scale, out=part, stream=stream)
+        a, b = merge_ev[n_step[0]]
+        n_step[0] += 1
+        a.record(stream)
+        A.merge(parts, out=(o, to, lse, tlse), stream=stream)
+        b.record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -191,21 +215,44 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-    roofline = {
-        "bound": "mfma",
-        "achieved": round(achieved, 2),
-        "peak": peak,
-        "unit": "TFLOP/s",
-        "frac": round(achieved / peak, 4),
-        "traffic": None if args.frozen_context else measured_traffic(w.name),
-        "kernel": (f"attn_jvp_bf16_kernel<{w.d}, {str(args.frozen_context).lower()}>" if w.dtype == "bf16"
-                   else f"attn_jvp_fp32_kernel<{w.d}>"),
-        "avg_launch_ms": round(avg_launch_ms, 4),
-        "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4),
-        "min_launch_ms": round(launch_ms[0], 4),
-        "algorithmic_flops_per_launch": flops,
-        "algorithmic_bytes_per_launch": w.algorithmic_bytes,
-    }
+    if args.split:
+        # the merge launch: n partial (O, tO, lse, tlse) rows read, one written
+        timed = merge_ev[args.warmup:]
+        merge_ms = sorted(a.elapsed_time(b) for a, b in timed)
+        avg_merge_ms = sum(merge_ms) / len(merge_ms)
+        rows = w.B * w.H * w.Lq
+        row_bytes = 2 * w.d * w.elem_bytes + 8
+        merge_bytes = float(rows * row_bytes * (len(bounds) + 1))
+        roofline = {
+            "bound": "hbm",
+            "achieved": round(merge_bytes / (avg_merge_ms * 1e-3) / 1e9, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(merge_bytes / (avg_merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "kernel": f"merge_kernel<{str(w.dtype == 'bf16').lower()}, {w.d}>",
+            "avg_launch_ms": round(avg_merge_ms, 4),
+            "median_launch_ms": round(merge_ms[len(merge_ms) // 2], 4),
+            "min_launch_ms": round(merge_ms[0], 4),
+            "algorithmic_bytes_per_launch": merge_bytes,
+            "shard_bounds": bounds,
+        }
+    else:
+        roofline = {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None if args.frozen_context else measured_traffic(w.name),
+            "kernel": (f"attn_jvp_bf16_kernel<{w.d}, {str(args.frozen_context).lower()}>" if w.dtype == "bf16"
+                       else f"attn_jvp_fp32_kernel<{w.d}>"),
+            "avg_launch_ms": round(avg_launch_ms, 4),
+            "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4),
+            "min_launch_ms": round(launch_ms[0], 4),
+            "algorithmic_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": w.algorithmic_bytes,
+        }
     out = {
         "metric": METRIC_FROZEN if args.frozen_context else METRIC,
         "value": round(value, 2),
@@ -221,8 +268,9 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "d": w.d,
                    "scale": w.scale, "parallelism": "single GPU",
-                   "path": "frozen context (tk = tv = NULL; 8 executed flops per logit and head dim)"
-                   if args.frozen_context else "full JVP (12 flops per logit and head dim)"},
+                   "path": ("frozen context (tk = tv = NULL; 8 executed flops per logit and head dim)"
+                            if args.frozen_context else "full JVP (12 flops per logit and head dim)")
+                   + (f"; {args.split} key shards + exact merge" if args.split else "")},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "wall_s_timed_region": round(wall, 3),
         "roofline": roofline,

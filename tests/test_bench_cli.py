@@ -22,3 +22,9 @@ def test_frozen_context_needs_zero_key_tangents():
     r = bench("--workload", "video_self_bf16", "--frozen-context")
     assert r.returncode == 2
     assert "tK = tV = 0" in r.stderr
+
+
+def test_split_part_count_is_checked():
+    r = bench("--split", "17")
+    assert r.returncode == 2
+    assert "--split" in r.stderr
