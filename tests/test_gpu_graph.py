@@ -1,0 +1,88 @@
+"""The C-ABI calls inside a captured HIP graph (torch.cuda.CUDAGraph on ROCm).
+
+Every entry point only enqueues kernels on the caller's stream and allocates
+nothing, so it can be captured.  The graph is replayed several times with the
+program's own eager work and synchronisations between replays, and every
+replay is compared with the eager result: bit-identical (same kernels, same
+inputs).
+"""
+import pytest
+import torch
+
+from workloads import custom_workload
+
+from _parity import device_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def A():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_forward_mode_attn_amd as A
+
+    A.load_library()
+    return A
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64)])
+def test_fwd_replays_in_a_graph(A, dtype, d):
+    w = custom_workload(2, 3, 300, 257, d, dtype, seed_id=7000 + d)
+    print(f"case graph fwd {dtype} d{d}", flush=True)
+    x = device_inputs(w)
+    args = (x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"])
+    ref = [t.clone() for t in A.fwd(*args, scale=w.scale)]
+    out = (torch.empty_like(x["q"]), torch.empty_like(x["q"]),
+           torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device=x["q"].device))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the capture stream
+        A.fwd(*args, scale=w.scale, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        A.fwd(*args, scale=w.scale, out=out)
+    for i in range(4):
+        for t in out:
+            t.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(out, ref):
+            assert torch.equal(got, want), i
+
+
+def test_split_and_merge_replay_in_a_graph(A):
+    w = custom_workload(1, 2, 200, 700, 128, "bf16", seed_id=7100)
+    print("case graph split + merge", flush=True)
+    x = device_inputs(w)
+    args = (x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"])
+    bounds = A.shard_bounds(w.Lk, 3)
+    ref = [t.clone() for t in A.merge([A.fwd_part(*args, a, b, scale=w.scale) for a, b in bounds])]
+    parts = [tuple(torch.empty_like(t) for t in ref) for _ in bounds]
+    out = tuple(torch.empty_like(t) for t in ref)
+
+    def body():
+        for (a, b), part in zip(bounds, parts):
+            A.fwd_part(*args, a, b, scale=w.scale, out=part)
+        A.merge(parts, out=out)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        body()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    for i in range(3):
+        for t in out:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(out, ref):
+            assert torch.equal(got, want), i

@@ -199,3 +199,20 @@ def test_rising_logits_frozen_and_split(A):
     print(f"  tlse {res['tlse']:.3e}", flush=True)
     check(w, res)
     assert res["tlse"] <= TOL[w.dtype]
+
+
+GRIDS = [
+    # (B, H, Lq, Lk, d, dtype): grid shapes far from the workloads'
+    (4, 32, 1, 4096, 128, "bf16"),   # decode-like: one query row per head, many heads
+    (1, 1, 1, 32760, 128, "bf16"),   # one query against the longest key sequence
+    (1, 1, 4096, 1, 64, "bf16"),     # many queries, a single key
+    (8, 64, 16, 96, 64, "fp32"),     # many tiny heads
+]
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,d,dtype", GRIDS)
+def test_grid_shapes(A, B, H, Lq, Lk, d, dtype):
+    w = custom_workload(B, H, Lq, Lk, d, dtype, seed_id=6000 + Lq + Lk)
+    print(f"case grid B{B} H{H} Lq{Lq} Lk{Lk} d{d} {dtype}", flush=True)
+    _, o, to, lse = run(A, w)
+    check(w, compare(w, o, to, lse))
