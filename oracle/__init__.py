@@ -4,3 +4,4 @@ Only the tests, the graft smoke check and the benchmark's cpu_baseline leg may
 import this package.  The product library never does.
 """
 from .attn_jvp import attention_jvp, attention_jvp_head, merge_shards  # noqa: F401
+from .proj import projection_jvp  # noqa: F401

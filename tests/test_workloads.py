@@ -89,3 +89,24 @@ def test_key_ramp_scales_key_rows_only():
     assert np.array_equal(k1, k0 * (1 + 0.25 * np.arange(40, dtype=np.float32))[:, None])
     for t in ("q", "v", "tq", "tk", "tv"):
         assert np.array_equal(head_array(flat, t, 0, 0), head_array(ramp, t, 0, 0))
+
+
+def test_projection_inputs_are_seeded_bf16_values():
+    import numpy as np
+
+    from workloads import PROJ_WORKLOADS, bf16_bits_to_f32, custom_proj, f32_to_bf16_bits, proj_array, proj_host_inputs
+
+    w = custom_proj(2, 33, 256, 3, 2, 64, seed_id=91)
+    a, b = proj_host_inputs(w), proj_host_inputs(w)
+    for t in ("x", "tx", "w", "bias"):
+        assert np.array_equal(a[t], b[t]) and a[t].shape == w.shape(t)
+        assert np.array_equal(bf16_bits_to_f32(f32_to_bf16_bits(a[t])), a[t])  # exactly bf16 values
+    assert not np.array_equal(a["x"][0], a["x"][1]) and not np.array_equal(a["x"], a["tx"])
+    assert abs(a["w"].std() * np.sqrt(w.D) - 1.0) < 0.02 and abs(a["bias"].std() - 0.1) < 0.02
+    assert np.array_equal(proj_array(w, "x", 1), a["x"][1])
+    frozen = custom_proj(1, 4, 64, 2, 1, 64, tangent=False, bias=False)
+    f = proj_host_inputs(frozen)
+    assert f["tx"] is None and f["bias"] is None
+    video = PROJ_WORKLOADS["qkv_video_bf16"]
+    assert video.F == 15360 and video.D == video.H * video.d
+    assert video.flops == 4.0 * 32760 * 5120 * 15360

@@ -14,3 +14,12 @@ from .inputs import (  # noqa: F401
     sample_rows,
     tq_head_scale,
 )
+from .proj import (  # noqa: F401
+    PROJ_TENSORS,
+    PROJ_WORKLOADS,
+    ProjWorkload,
+    custom_proj,
+    proj_array,
+    proj_host_inputs,
+    proj_upload,
+)

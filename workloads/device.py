@@ -27,3 +27,26 @@ def device_inputs(w, device="cuda", threads=8):
                 else torch.from_numpy(arr)
             out[t][b, h].copy_(src)
     return out
+
+
+def device_proj_inputs(w, device="cuda"):
+    """The projection inputs of ``w`` on ``device`` as bf16 tensors: x, tx
+    [B, L, D] (tx None without tangent), w [F, D], bias [F] (None without bias)."""
+    import torch
+
+    from .proj import proj_upload
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
+
+    out = {"x": torch.empty(w.shape("x"), dtype=torch.bfloat16, device=device)}
+    for b in range(w.B):
+        out["x"][b].copy_(up(proj_upload(w, "x", b)))
+    out["tx"] = None
+    if w.tangent:
+        out["tx"] = torch.empty(w.shape("tx"), dtype=torch.bfloat16, device=device)
+        for b in range(w.B):
+            out["tx"][b].copy_(up(proj_upload(w, "tx", b)))
+    out["w"] = up(proj_upload(w, "w"))
+    out["bias"] = up(proj_upload(w, "bias")) if w.bias else None
+    return out
