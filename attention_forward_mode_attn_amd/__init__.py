@@ -4,7 +4,8 @@ The functions below carry the C ABI's names and only marshal arguments; every
 step of the computation runs in the HIP kernels of the library.  ``fwd`` is a
 convenience wrapper that allocates the outputs with torch and raises on error;
 ``fwd_part``, ``merge`` and ``fwd_split`` do the same for the key-sharded
-partial passes and their exact merge.
+partial passes and their exact merge, and ``proj`` for the projection of
+hidden states into attention heads with its tangent.
 There is no fallback: if the library is missing, every call raises.
 """
 from __future__ import annotations
@@ -16,8 +17,8 @@ __all__ = [
     "ATTN_JVP_FP32", "ATTN_JVP_BF16", "ATTN_JVP_OK", "ATTN_JVP_EINVAL", "ATTN_JVP_EUNSUPPORTED",
     "ATTN_JVP_EALIGN", "ATTN_JVP_ELAUNCH", "ATTN_JVP_MAX_MERGE_PARTS", "AttnJvpError", "attn_jvp_fwd",
     "attn_jvp_fwd_part", "attn_jvp_merge", "attn_jvp_status_string", "attn_jvp_last_error",
-    "attn_jvp_version", "fwd", "fwd_part", "merge", "fwd_split", "shard_bounds", "library_path",
-    "load_library",
+    "attn_jvp_version", "attn_jvp_proj", "fwd", "fwd_part", "merge", "fwd_split", "shard_bounds", "proj",
+    "library_path", "load_library",
 ]
 
 ATTN_JVP_FP32, ATTN_JVP_BF16 = 0, 1
@@ -58,6 +59,8 @@ def load_library() -> ctypes.CDLL:
     lib.attn_jvp_fwd_part.restype = ctypes.c_int
     lib.attn_jvp_merge.argtypes = [ctypes.c_int] + [ctypes.POINTER(vp)] * 4 + [vp] * 4 + [i64] * 2 + [ctypes.c_int, vp]
     lib.attn_jvp_merge.restype = ctypes.c_int
+    lib.attn_jvp_proj.argtypes = [vp] * 6 + [i64] * 6 + [ctypes.c_int, vp]
+    lib.attn_jvp_proj.restype = ctypes.c_int
     lib.attn_jvp_status_string.argtypes = [ctypes.c_int]
     lib.attn_jvp_status_string.restype = ctypes.c_char_p
     lib.attn_jvp_last_error.argtypes = []
@@ -112,6 +115,16 @@ def attn_jvp_merge(n, o_parts, to_parts, lse_parts, tlse_parts, o, to, lse, tlse
     return int(lib.attn_jvp_merge(
         int(n), arr(o_parts), arr(to_parts), arr(lse_parts), arr(tlse_parts),
         _ptr(o), _ptr(to), _ptr(lse), _ptr(tlse), int(rows), int(d), int(dtype), stream,
+    ))
+
+
+def attn_jvp_proj(x, tx, w, bias, y, ty, B, L, D, n_out, H, d, dtype, stream=None) -> int:
+    """Marshal to the C entry point (tx, bias, ty may be None).  Returns the
+    status code."""
+    lib = load_library()
+    return int(lib.attn_jvp_proj(
+        _ptr(x), _ptr(tx), _ptr(w), _ptr(bias), _ptr(y), _ptr(ty),
+        int(B), int(L), int(D), int(n_out), int(H), int(d), int(dtype), stream,
     ))
 
 
@@ -252,3 +265,40 @@ def fwd_split(q, k, v, tq, tk, tv, n_split, scale=None, stream=None):
     parts = [fwd_part(q, k, v, tq, tk, tv, a, b, scale=scale, stream=stream)
              for a, b in shard_bounds(k.shape[2], n_split)]
     return merge(parts, stream=stream)
+
+
+def proj(x, tx, w, bias=None, n_out=3, heads=None, out=None, stream=None):
+    """Y = x W^T + bias and TY = tx W^T for bfloat16 torch tensors x, tx
+    [B, L, D] (tx None: no tangent), w [n_out*heads*d, D], bias [n_out*heads*d]
+    or None; returns (y, ty), each [n_out, B, heads, L, d] (ty None without
+    tangent), so that y[0], y[1], y[2] are the q, k, v of ``fwd`` for n_out = 3.
+    ``out=(y, ty)`` reuses buffers."""
+    import torch
+
+    if heads is None:
+        raise ValueError("heads is required")
+    if x.dtype != torch.bfloat16:
+        raise TypeError("the projection takes bfloat16 tensors")
+    ins = [t for t in (x, tx, w, bias) if t is not None]
+    if any(t.dtype != x.dtype or t.device != x.device or not t.is_contiguous() for t in ins):
+        raise ValueError("all inputs: bfloat16, one device, contiguous")
+    if x.dim() != 3 or (tx is not None and tx.shape != x.shape):
+        raise ValueError("x and tx must be [B, L, D]")
+    B, L, D = x.shape
+    F = w.shape[0]
+    if w.dim() != 2 or w.shape[1] != D or F % (n_out * heads) != 0:
+        raise ValueError("w must be [n_out*heads*d, D]")
+    d = F // (n_out * heads)
+    if bias is not None and bias.shape != (F,):
+        raise ValueError("bias must be [n_out*heads*d]")
+    shape = (n_out, B, heads, L, d)
+    if out is None:
+        y = torch.empty(shape, dtype=x.dtype, device=x.device)
+        ty = torch.empty(shape, dtype=x.dtype, device=x.device) if tx is not None else None
+    else:
+        y, ty = out
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    status = attn_jvp_proj(x, tx, w, bias, y, ty, B, L, D, n_out, heads, d, ATTN_JVP_BF16, s.cuda_stream)
+    if status != ATTN_JVP_OK:
+        raise AttnJvpError(status, attn_jvp_last_error())
+    return y, ty

@@ -143,4 +143,35 @@ int attn_jvp_merge(int n, const void* const* o_parts, const void* const* to_part
   return ATTN_JVP_OK;
 }
 
+int attn_jvp_proj(const void* x, const void* tx, const void* w, const void* bias, void* y, void* ty, int64_t B,
+                  int64_t L, int64_t D, int64_t n_out, int64_t H, int64_t d, int dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (dtype != ATTN_JVP_FP32 && dtype != ATTN_JVP_BF16) return fail(ATTN_JVP_EINVAL, "dtype must be 0 (fp32) or 1 (bf16)");
+  if (B < 0 || L < 0 || D < 0 || n_out < 0 || H < 0 || d < 0) return fail(ATTN_JVP_EINVAL, "negative size");
+  if (dtype != ATTN_JVP_BF16) return fail(ATTN_JVP_EUNSUPPORTED, "the projection is bf16 only");
+  if (d != 64 && d != 128) return fail(ATTN_JVP_EUNSUPPORTED, "head dimension must be 64 or 128");
+  if (B == 0 || L == 0 || n_out == 0 || H == 0) return ATTN_JVP_OK;  // nothing to compute
+  if (D == 0 || D % 64 != 0) return fail(ATTN_JVP_EUNSUPPORTED, "D must be a positive multiple of 64");
+  if (!x || !w || !y) return fail(ATTN_JVP_EINVAL, "NULL pointer");
+  if ((tx == nullptr) != (ty == nullptr)) return fail(ATTN_JVP_EINVAL, "tx and ty must both be NULL or both non-NULL");
+  const void* p16[] = {x, tx, w, bias, y, ty};
+  for (const void* q : p16)
+    if (!aligned(q, 16)) return fail(ATTN_JVP_EALIGN, "pointers must be 16-byte aligned");
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t F = n_out * H * d;
+  if (n_out >= lim || H >= lim || F >= lim || L * D >= lim || F * D >= lim || L * d >= lim || D >= (int64_t(1) << 22))
+    return fail(ATTN_JVP_EUNSUPPORTED, "size beyond the projection's limits");
+  const int64_t blocks = ((F + 255) / 256) * ((L + 127) / 128) * B;
+  if (B >= lim || blocks >= lim) return fail(ATTN_JVP_EUNSUPPORTED, "too many workgroups");
+  attnjvp::ProjProblem p;
+  p.x = x; p.tx = tx; p.w = w; p.bias = bias; p.y = y; p.ty = ty;
+  p.B = (int)B; p.L = (int)L; p.D = (int)D; p.n_out = (int)n_out; p.H = (int)H; p.d = (int)d;
+  const hipError_t e = attnjvp::launch_proj(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    std::snprintf(g_last_error, sizeof g_last_error, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+    return ATTN_JVP_ELAUNCH;
+  }
+  return ATTN_JVP_OK;
+}
+
 }  // extern "C"

@@ -14,12 +14,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace attnjvp {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaveRows = 32;              // query rows per wave
 constexpr int kWaves = 4;                  // waves per workgroup
@@ -36,6 +41,35 @@ constexpr float kLn2 = 0.6931471805599453f;
 // the row max flush to zero.  A large slack keeps peaky softmaxes (logit std
 // ~8) from leaving the hot loop to rescale on most tiles.
 constexpr float kRescaleSlack = 32.0f;
+
+__device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// Two floats to a packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ inline unsigned pack_bf16(float a, float b) {
+  f32x2 f = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+}
+
+// Scheduling fence: the compiler may not move instructions across it.  The
+// pipelined loops are written as sequences of small units (one MFMA plus a
+// slice of independent work) separated by fences, so that the vector ALU and
+// the memory pipes work while the matrix core runs instead of the two
+// alternating in long runs.
+__device__ inline void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+template <int I>
+using IC = std::integral_constant<int, I>;
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E).  Every
+// register-array index in a pipelined loop is a constant, so the arrays stay
+// in registers (a runtime index would send them to memory).
+template <int B, int E, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // Buffer resource over [base, base + bytes): loads past the end return 0 and
 // stores past the end are dropped by the hardware range check.
@@ -62,6 +96,12 @@ __device__ inline void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, float 
 // passed in M0.
 __device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff) {
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(lds_addr) : "memory");
+}
+// The same with a wave-uniform byte offset in the scalar offset field.  The
+// buffer range check covers the sum of the vector and scalar offsets, so
+// bytes past the resource still read as zero.
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(voff), "s"(r), "s"(soff), "{m0}"(lds_addr) : "memory");
 }
 
 // LDS byte address of a __shared__ object.

@@ -34,17 +34,11 @@
 //  * variants: a frozen context (tK = tV = 0) skips the tK and tV products
 //    and copies; a key shard (kv_rows > Lk) is the same pass on part of the
 //    keys, with the tangent of lse as an extra output for an exact merge.
-#include <type_traits>
-
 #include "device_common.h"
 #include "launch.h"
 
 namespace attnjvp {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBc = 64;  // keys per tile
 
@@ -114,13 +108,6 @@ __device__ inline i16x4 lds_tr16(const char* p) {
       (__attribute__((address_space(3))) i16x4*)(__attribute__((address_space(3))) const char*)p);
 }
 
-__device__ inline bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
-
-__device__ inline unsigned pack_bf16(float a, float b) {
-  f32x2 f = {a, b};
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
-}
-
 // c + x.lo + x.hi for a packed bf16 pair x (fp32 arithmetic).
 __device__ inline float sum_bf16x2(unsigned x, float c) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -131,12 +118,6 @@ __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Scheduling fence: the compiler may not move instructions across it.  The
-// pipelined iteration is written as a sequence of small units (one MFMA plus a
-// slice of independent VALU work) separated by fences, so that the vector ALU
-// works while the matrix core runs instead of the two alternating in long runs.
-__device__ inline void fence() { __builtin_amdgcn_sched_barrier(0); }
-
 // Keep a value computed here.  Values that are only used in the next
 // iteration (the running sums, the logits waiting for their softmax) would
 // otherwise be sunk by the optimizer past the fences to the loop latch, where
@@ -144,19 +125,6 @@ __device__ inline void fence() { __builtin_amdgcn_sched_barrier(0); }
 __device__ inline void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ inline void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
 
-template <int I>
-using IC = std::integral_constant<int, I>;
-
-// Compile-time loop: f(std::integral_constant<int, i>) for i in [B, E).  Every
-// register-array index in the pipelined loop is a constant, so the arrays stay
-// in registers (a runtime index would send them to memory).
-template <int B, int E, typename F>
-__device__ inline void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
 
 // kFrozen: the key-side tangents are zero (tK = tV = 0, a frozen context):
 // the tK Q^T and tV P^T products and the tK/tV tile copies are skipped.

@@ -43,4 +43,16 @@ struct MergeProblem {
 
 hipError_t launch_merge(const MergeProblem& p, hipStream_t stream);
 
+struct ProjProblem {
+  const void* x;
+  const void* tx;    // null: no tangent (ty null too)
+  const void* w;
+  const void* bias;  // may be null
+  void* y;
+  void* ty;
+  int B, L, D, n_out, H, d;  // validated: d in {64, 128}, D % 64 == 0, B*L > 0, n_out*H > 0
+};
+
+hipError_t launch_proj(const ProjProblem& p, hipStream_t stream);
+
 }  // namespace attnjvp

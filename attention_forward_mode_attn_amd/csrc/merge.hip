@@ -23,13 +23,11 @@
 #include <cmath>
 #include <cstdint>
 
+#include "device_common.h"
 #include "launch.h"
 
 namespace attnjvp {
 namespace {
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct MergeArgs {
   MergeProblem p;
@@ -37,15 +35,6 @@ struct MergeArgs {
 
 __device__ inline float bf16_lo(unsigned x) { return __uint_as_float(x << 16); }
 __device__ inline float bf16_hi(unsigned x) { return __uint_as_float(x & 0xFFFF0000u); }
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Two floats to a packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ inline unsigned pack_bf16(float a, float b) {
-  f32x2 f = {a, b};
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
-}
 
 template <bool BF16>
 __device__ inline void load8(const void* base, size_t elem, float (&x)[8]) {

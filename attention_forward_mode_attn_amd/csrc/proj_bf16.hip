@@ -1,0 +1,312 @@
+// Projection of hidden states into attention heads, with its tangent, on gfx950
+// matrix cores (v_mfma_f32_32x32x16_bf16):
+//
+//   Y = X W^T + b,   TY = TX W^T,   feature f = (n*H + h)*d + j of token t of
+//   batch b written to [n, b, h, t, j] (the layout the attention kernel reads).
+//
+// The rCM pages make every layer take and return tangents and hand the Q, K, V
+// tangents to attention laid out like Q, K, V (ai.info summary of "Large Scale
+// Diffusion Distillation via Score-Regularized Continuous-Time Consistency",
+// "Methodology in Plain English").  The layer in front of attention is read as
+// a linear map; its JVP is the same weight applied to the tangent, so one pass
+// computes both products from every weight tile it stages:
+//
+//  * one workgroup = 4 waves = 256 output features x 128 tokens of one batch;
+//    wave w owns tokens 32w .. 32w + 31 and all 256 features, for X and TX:
+//    16 accumulators of 32 x 32 (all 256 accumulation registers);
+//  * the products are transposed, Y^T = W X^T (features in the MFMA M slot,
+//    tokens in N), so a lane owns one token and the epilogue stores runs of 8
+//    consecutive features of one head;
+//  * the hidden dimension streams in steps of 64 through double-buffered LDS
+//    (W | X | TX tiles, 64 KB per stage) by buffer_load ... lds, rows of 128
+//    bytes with XOR-swizzled 16-byte units; each W fragment read from LDS
+//    feeds two MFMAs (X and TX);
+//  * software pipeline per step: fenced units of one MFMA each, the next
+//    step's copies issued in the first units and the fragment reads a few units
+//    ahead of their use.  The barrier that publishes the next step's tiles sits
+//    near the end of the step, after the last read of the current stage, so
+//    the next step's first fragments are read before the step ends and no step
+//    starts by waiting on LDS;
+//  * the bias initialises the X accumulators; the epilogue rounds to bf16 and
+//    stores 16 bytes per lane after pairing the half-waves with v_permlane32_swap.
+//  * kTangent = false (a frozen input, no TX): X tiles and accumulators only.
+#include "device_common.h"
+#include "launch.h"
+
+namespace attnjvp {
+namespace {
+
+constexpr int kTF = 256;                       // output features per workgroup
+constexpr int kTT = kWaves * kWaveRows;        // tokens per workgroup (128)
+constexpr int kTK = 64;                        // hidden-dim elements per step
+constexpr int kRowB = kTK * 2;                 // bytes of one tile row
+constexpr int kWTile = kTF * kRowB;            // 32 KB
+constexpr int kXTile = kTT * kRowB;            // 16 KB
+constexpr int kStageB = kWTile + 2 * kXTile;   // W | X | TX
+constexpr int kFB = kTF / 32;                  // 32-feature blocks per tile
+constexpr int kGroupF = 8;                     // feature tiles per dispatch group
+constexpr int kRing = 8;                       // W fragment registers in flight
+
+struct ProjParams {
+  const void* x;
+  const void* tx;
+  const void* w;
+  const void* bias;
+  void* y;
+  void* ty;
+  int B, L, D, F, H, d;
+  int n_ft, n_tt, n_blocks;
+};
+
+// Unit u (16 bytes) of tile row r sits at slot u ^ swz(r): the 16 lanes that a
+// ds_read_b128 serves together read one unit column of 16 consecutive rows,
+// and the swizzle spreads them over all 16 bank groups of the 64-bank LDS.
+__device__ inline int swz(int r) { return (r >> 1) & 7; }
+
+__device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Per-lane global offset of one 1 KB slice (8 rows x 128 bytes) of a tile whose
+// rows are D elements apart: lane l fills LDS bytes 16l of the slice, i.e. row
+// 8s + l/8, slot l%8, which holds unit (l%8) ^ swz(row) of that row.
+__device__ inline uint32_t slice_voff(int s, int lane, int D) {
+  const int r = 8 * s + lane / 8;
+  const int u = (lane % 8) ^ swz(r);
+  return (uint32_t)r * (uint32_t)D * 2u + (uint32_t)u * 16u;
+}
+
+// Schedule of one step (see the file comment).  W fragment q = 8c + fb (hidden
+// chunk c of 16, feature block fb) is used by units q*kPer .. q*kPer + kPer - 1.
+template <bool kT>
+struct Sched {
+  static constexpr int kPer = kT ? 2 : 1;                   // MFMAs per W fragment
+  static constexpr int kUnits = 32 * kPer;                  // MFMAs per step and wave
+  static constexpr int kLead = kT ? 8 : 5;                  // W read this many units before use
+  static constexpr int kPre = (kLead + kPer - 1) / kPer;    // W fragments read in the previous step
+  static constexpr int kXLead = kT ? 10 : 7;                // X read units before chunk c starts
+  static constexpr int kBar = kT ? 56 : 27;                 // unit of the mid-step barrier
+  static constexpr int kNX = kT ? 2 : 1;                    // X fragments per chunk (X, TX)
+  static constexpr int kDma = ((kWTile + kNX * kXTile) / 1024) / kWaves;  // slices per wave
+  static constexpr int kWDma = kWTile / 1024 / kWaves;                    // of which W
+  static_assert(31 * kPer - kLead < kBar, "current-stage W reads end before the barrier");
+  static_assert(3 * 8 * kPer - kXLead + kNX - 1 < kBar, "current-stage X reads end before the barrier");
+  static_assert(kDma <= kBar, "copies issued before the barrier");
+  // unit of the i-th next-stage read (X fragments first, then W 0 .. kPre - 1);
+  // reads that do not fit go to the last unit
+  static constexpr int next_unit(int i) { return kBar + i < kUnits ? kBar + i : kUnits - 1; }
+  // every next-stage W fragment is read at least 4 units before its first use
+  static_assert(kUnits - next_unit(kNX + kPre - 1) + (kPre - 1) * kPer >= 4, "next-stage lead");
+  static_assert(kUnits - next_unit(kNX) >= 4, "next-stage lead of W fragment 0");
+};
+
+template <bool kT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void proj_bf16_kernel(ProjParams p) {
+  using S = Sched<kT>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageB];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, n = lane & 31, hh = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+
+  // Dispatch order: the logical blocks of one XCD are contiguous, and within
+  // them groups of kGroupF feature tiles sweep the token tiles together, so the
+  // workgroups running at once on an XCD share W and X tiles in its L2.
+  const int l = xcd_logical_block(blockIdx.x, p.n_blocks);
+  const int n_t = p.n_tt * p.B;
+  const int group = l / (kGroupF * n_t);
+  const int first_ft = group * kGroupF;
+  const int gsz = min(p.n_ft - first_ft, kGroupF);
+  const int r_in = l - group * kGroupF * n_t;
+  const int ft = first_ft + r_in % gsz;
+  const int tg = r_in / gsz;
+  const int b = tg / p.n_tt, tt = tg % p.n_tt;
+  const int f0 = ft * kTF, t0 = tt * kTT;
+  const int D = p.D, L = p.L, F = p.F;
+
+  // Resources: rows past F (features) or past L (tokens) read as zero.
+  const size_t xoff = ((size_t)b * L + t0) * D * 2;
+  const auto rw = make_rsrc((const char*)p.w + (size_t)f0 * D * 2, (uint32_t)(F - f0) * (uint32_t)D * 2u);
+  const auto rx = make_rsrc((const char*)p.x + xoff, (uint32_t)(L - t0) * (uint32_t)D * 2u);
+  const auto rtx = make_rsrc(kT ? (const char*)p.tx + xoff : (const char*)p.x, kT ? (uint32_t)(L - t0) * (uint32_t)D * 2u : 0u);
+
+  // This wave's copy slices: W slices 8wv .. 8wv + 7, X (and TX) slices 4wv .. 4wv + 3.
+  uint32_t voff[S::kDma];
+#pragma unroll
+  for (int i = 0; i < S::kDma; ++i) {
+    const int wi = i < S::kWDma ? i : (i - S::kWDma) % 4;
+    voff[i] = slice_voff(i < S::kWDma ? S::kWDma * wv + wi : 4 * wv + wi, lane, D);
+  }
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_address(smem));
+  // copy slice i of this wave for step k into stage k & 1
+  auto issue = [&](int k, auto ii) {
+    constexpr int i = decltype(ii)::value;
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)k * kRowB);
+    const uint32_t st = smem_lds + (k & 1) * kStageB;
+    if constexpr (i < S::kWDma) {
+      lds_dma16(rw, st + (S::kWDma * wv + i) * 1024, voff[i], soff);
+    } else if constexpr (i < S::kWDma + 4) {
+      lds_dma16(rx, st + kWTile + (4 * wv + i - S::kWDma) * 1024, voff[i], soff);
+    } else {
+      lds_dma16(rtx, st + kWTile + kXTile + (4 * wv + i - S::kWDma - 4) * 1024, voff[i], soff);
+    }
+  };
+
+  // Fragment offsets in a stage: W fragment (chunk c, block fb) of lane (n, hh)
+  // is row 32fb + n, unit 2c + hh; X fragment c is row 32wv + n of the X tile.
+  // Both rows have swz = (n >> 1) & 7.
+  uint32_t lo[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) lo[c] = n * kRowB + (((2 * c + hh) ^ swz(n)) << 4);
+  const int xrow = kWTile + wv * 32 * kRowB;
+
+  // Accumulators: X products start from the bias (register r of block fb holds
+  // feature f0 + 32fb + 8(r/4) + 4hh + r%4), TX products from zero.
+  f32x16 acc[2][kFB];
+  {
+    const auto rb = make_rsrc(p.bias ? (const char*)p.bias + (size_t)f0 * 2 : (const char*)p.x,
+                              p.bias ? (uint32_t)(F - f0) * 2u : 0u);
+#pragma unroll
+    for (int fb = 0; fb < kFB; ++fb) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rb, (32 * fb + 8 * g + 4 * hh) * 2, 0, 0);
+        acc[0][fb][4 * g + 0] = __uint_as_float(v[0] << 16);
+        acc[0][fb][4 * g + 1] = __uint_as_float(v[0] & 0xFFFF0000u);
+        acc[0][fb][4 * g + 2] = __uint_as_float(v[1] << 16);
+        acc[0][fb][4 * g + 3] = __uint_as_float(v[1] & 0xFFFF0000u);
+      }
+      acc[1][fb] = f32x16{};
+    }
+  }
+
+  bf16x8 wf[kRing], xf[2][2];
+  auto read_w = [&](const char* st, auto iq) {
+    constexpr int q = decltype(iq)::value;
+    wf[q % kRing] = *reinterpret_cast<const bf16x8*>(st + (q % 8) * 32 * kRowB + lo[q / 8]);
+  };
+  auto read_x = [&](const char* st, auto ic, auto iw) {
+    constexpr int c = decltype(ic)::value, which = decltype(iw)::value;
+    xf[c & 1][which] = *reinterpret_cast<const bf16x8*>(st + xrow + which * kXTile + lo[c]);
+  };
+
+  // One step: MFMAs on stage k & 1; with kMore, the copies of step k + 1, the
+  // barrier that publishes them, and the first reads of step k + 1.
+  auto step = [&](int k, auto more) {
+    constexpr bool kMore = decltype(more)::value;
+    const char* cur = smem + (k & 1) * kStageB;
+    const char* nxt = smem + ((k + 1) & 1) * kStageB;
+    static_for<0, S::kUnits>([&](auto iu) {
+      constexpr int u = decltype(iu)::value;
+      constexpr int q = u / S::kPer, c = q / 8, fb = q % 8, which = u % S::kPer;
+      acc[which][fb] = mfma(wf[q % kRing], xf[c & 1][which], acc[which][fb]);
+      if constexpr (kMore && u < S::kDma) issue(k + 1, IC<u>{});
+      // current stage: W fragment q2 read kLead units before its first use
+      static_for<S::kPre, 32>([&](auto iq) {
+        constexpr int q2 = decltype(iq)::value;
+        if constexpr (q2 * S::kPer - S::kLead == u) read_w(cur, iq);
+      });
+      static_for<1, 4>([&](auto ic) {
+        constexpr int c2 = decltype(ic)::value;
+        static_for<0, S::kNX>([&](auto iw) {
+          constexpr int w2 = decltype(iw)::value;
+          if constexpr (c2 * 8 * S::kPer - S::kXLead + w2 == u) read_x(cur, ic, iw);
+        });
+      });
+      if constexpr (kMore) {
+        if constexpr (u == S::kBar) {
+          __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0): copies landed, reads done
+          __syncthreads();
+        }
+        static_for<0, S::kNX>([&](auto iw) {
+          constexpr int w2 = decltype(iw)::value;
+          if constexpr (S::next_unit(w2) == u) read_x(nxt, IC<0>{}, iw);
+        });
+        static_for<0, S::kPre>([&](auto iq) {
+          constexpr int q2 = decltype(iq)::value;
+          if constexpr (S::next_unit(S::kNX + q2) == u) read_w(nxt, iq);
+        });
+      }
+      fence();
+    });
+  };
+
+  const int nk = D / kTK;
+  // prologue: step 0's tiles, then its first fragments
+  static_for<0, S::kDma>([&](auto ii) { issue(0, ii); });
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  static_for<0, S::kNX>([&](auto iw) { read_x(smem, IC<0>{}, iw); });
+  static_for<0, S::kPre>([&](auto iq) { read_w(smem, iq); });
+  for (int k = 0; k < nk - 1; ++k) step(k, std::true_type{});
+  step(nk - 1, std::false_type{});
+
+  // ---- epilogue ----------------------------------------------------------------
+  // Accumulator group g (registers 4g .. 4g + 3) of a lane holds features
+  // 8g + 4hh .. +3 of its block; groups 2gp and 2gp + 1 are paired across the
+  // half-waves so that each lane holds 8 consecutive features (half 0:
+  // 16gp .. +7, half 1: 16gp + 8 .. +15), one 16-byte store each.  Everything is
+  // packed before the first store.
+  auto pair = [](u32x2 x, u32x2 y) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
+    return u32x4{s0[0], s1[0], s0[1], s1[1]};
+  };
+  u32x4 pk[S::kNX][kFB][2];
+#pragma unroll
+  for (int w2 = 0; w2 < S::kNX; ++w2)
+#pragma unroll
+    for (int fb = 0; fb < kFB; ++fb)
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) {
+        u32x2 h2[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int g = 2 * gp + h;
+          h2[h] = u32x2{pack_bf16(acc[w2][fb][4 * g], acc[w2][fb][4 * g + 1]),
+                        pack_bf16(acc[w2][fb][4 * g + 2], acc[w2][fb][4 * g + 3])};
+        }
+        pk[w2][fb][gp] = pair(h2[0], h2[1]);
+      }
+  fence();
+  const int token = t0 + wv * 32 + n;  // rows at or past L fall outside the output range: dropped
+  const uint32_t obase = ((uint32_t)token * p.d + 8 * hh) * 2;
+  const int HD = p.H * p.d;
+#pragma unroll
+  for (int fb = 0; fb < kFB; ++fb) {
+    const int f = f0 + 32 * fb;
+    if (f >= F) break;  // wave-uniform: the partial last feature tile
+    const int np = f / HD, h = (f % HD) / p.d, j0 = f % p.d;
+    const size_t head = (((size_t)np * p.B + b) * p.H + h) * (size_t)L * p.d * 2;
+    const uint32_t hbytes = (uint32_t)L * p.d * 2u;
+#pragma unroll
+    for (int w2 = 0; w2 < S::kNX; ++w2) {
+      const auto ro = make_rsrc((const char*)(w2 ? p.ty : p.y) + head, hbytes);
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp)
+        __builtin_amdgcn_raw_buffer_store_b128(pk[w2][fb][gp], ro, obase, (j0 + 16 * gp) * 2, 0);
+    }
+  }
+}
+
+template <bool kT>
+hipError_t launch(const ProjProblem& pr, hipStream_t stream) {
+  ProjParams p;
+  p.x = pr.x; p.tx = pr.tx; p.w = pr.w; p.bias = pr.bias; p.y = pr.y; p.ty = pr.ty;
+  p.B = pr.B; p.L = pr.L; p.D = pr.D; p.H = pr.H; p.d = pr.d;
+  p.F = pr.n_out * pr.H * pr.d;
+  p.n_ft = (p.F + kTF - 1) / kTF;
+  p.n_tt = (p.L + kTT - 1) / kTT;
+  p.n_blocks = p.n_ft * p.n_tt * p.B;
+  hipLaunchKernelGGL((proj_bf16_kernel<kT>), dim3(p.n_blocks), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_proj(const ProjProblem& p, hipStream_t stream) {
+  return p.tx ? launch<true>(p, stream) : launch<false>(p, stream);
+}
+
+}  // namespace attnjvp

@@ -8,7 +8,12 @@ self-attention layer (B=1, H=40, Lq=Lk=32760, d=128, bf16).  Throughput counts
 the nominal 12*B*H*Lq*Lk*d flops of the six dense products.  Prints ONE JSON
 line on stdout.
 
-Extra modes used by the profiling recipes:
+Other modes:
+  --proj NAME          time attn_jvp_proj, the projection of hidden states into
+                       attention heads with its tangent, on a projection workload
+                       (qkv_video_bf16: 32760 tokens, D = 5120 -> 3 x 40 x 128);
+                       throughput counts 2*B*L*D*F flops per product (two with a
+                       tangent).  Same JSON contract.
   --copy-calibration   time/profile a plain device copy of known size (HBM
                        counter calibration) instead of the kernel.
 """
@@ -30,22 +35,25 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix/vector, vendor figure
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, vendor figure
 METRIC = "attention-JVP TFLOP/s (12*B*H*Lq*Lk*d) + % bf16 MFMA peak, 1 MI355X"
 METRIC_FROZEN = "attention-JVP executed TFLOP/s, frozen context (8*B*H*Lq*Lk*d) + % bf16 MFMA peak, 1 MI355X"
-# The sources of the bf16 kernel whose HBM traffic profiles/ records: a change
-# to any of them makes the recorded traffic stale (reported as null).
-KERNEL_SOURCES = ["attention_forward_mode_attn_amd/csrc/kernel_bf16.hip",
-                  "attention_forward_mode_attn_amd/csrc/device_common.h",
-                  "attention_forward_mode_attn_amd/csrc/launch.h"]
+METRIC_PROJ = "projection-JVP TFLOP/s (2*B*L*D*F per product, X and TX) + % bf16 MFMA peak, 1 MI355X"
+# The sources of each kernel whose HBM traffic profiles/ records: a change to
+# any of them makes the recorded traffic stale (reported as null).
+_CSRC = "attention_forward_mode_attn_amd/csrc/"
+KERNEL_SOURCES = {
+    "attention": [_CSRC + "kernel_bf16.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
+    "proj": [_CSRC + "proj_bf16.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "attention") -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kernel: str = "attention"):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None
     when there is none for this workload or the kernel changed since."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
@@ -54,9 +62,18 @@ def measured_traffic(workload: str):
     txt = open(path).read()
     m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
     m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m_src or not m_b or m_src.group(1) != kernel_source_hash():
+    if not m_src or not m_b or m_src.group(1) != kernel_source_hash(kernel):
         return None
     return float(m_b.group(1))
+
+
+def _blas_cores() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max((int(x.get("num_threads", 1)) for x in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
 
 
 def cpu_baseline(w, budget_s: float = 30.0, rows_per_head: int = 1024):
@@ -70,12 +87,7 @@ def cpu_baseline(w, budget_s: float = 30.0, rows_per_head: int = 1024):
     from oracle import attention_jvp_head
     from workloads import TENSORS, head_array, sample_rows
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max((int(x.get("num_threads", 1)) for x in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    cores = _blas_cores()
     rows_done = 0
     t_total = 0.0
     heads = 0
@@ -106,6 +118,112 @@ def cpu_baseline(w, budget_s: float = 30.0, rows_per_head: int = 1024):
     }
 
 
+def cpu_baseline_proj(w, h, budget_s: float = 30.0):
+    """Time the fp64 projection oracle on growing blocks of tokens (all
+    features) until the budget is spent; ``h`` holds the host inputs."""
+    from oracle import projection_jvp
+
+    n = 64
+    rows_done, t_total = 0, 0.0
+    while t_total < budget_s and rows_done < w.L:
+        rows = list(range(rows_done, min(w.L, rows_done + n)))
+        t0 = time.perf_counter()
+        projection_jvp(h["x"], h["tx"], h["w"], h["bias"], w.n_out, w.H, w.d, rows=rows)
+        t_total += time.perf_counter() - t0
+        rows_done += len(rows)
+        n *= 2
+    tok = rows_done * w.B
+    flops = 2.0 * (2 if w.tangent else 1) * tok * w.D * w.F
+    full_s = t_total / tok * (w.B * w.L)
+    return {
+        "value": flops / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": _blas_cores(),
+        "kind": "oracle",
+        "sample": f"{tok} tokens ({rows_done} per batch x {w.B}) of {w.name}, all {w.F} features; "
+                  f"{t_total:.1f} s; full workload extrapolates to {full_s:.0f} s",
+        "float": "f64",
+    }
+
+
+def bench_proj(args):
+    import torch
+
+    import attention_forward_mode_attn_amd as A
+    from workloads import PROJ_WORKLOADS, proj_host_inputs
+    from workloads.device import device_proj_inputs
+
+    w = PROJ_WORKLOADS[args.proj]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"bench: {w.name} B{w.B} L{w.L} D{w.D} n_out{w.n_out} H{w.H} d{w.d} tangent={w.tangent}: "
+          "generating inputs", file=sys.stderr, flush=True)
+    x = device_proj_inputs(w)
+    y = torch.empty(w.out_shape, dtype=torch.bfloat16, device=dev)
+    ty = torch.empty_like(y) if w.tangent else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        A.proj(x["x"], x["tx"], x["w"], x["bias"], n_out=w.n_out, heads=w.H, out=(y, ty), stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for a, b in per:
+        a.record(stream)
+        step()
+        b.record(stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    launch_ms = sorted(a.elapsed_time(b) for a, b in per)
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (avg_launch_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC_PROJ,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) hidden states and tangents, N(0,1/D) weights, N(0,0.1^2) bias)",
+        "config": {"workload": w.name, "B": w.B, "L": w.L, "D": w.D, "n_out": w.n_out, "H": w.H, "d": w.d,
+                   "tangent": w.tangent, "bias": w.bias, "parallelism": "single GPU"},
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "wall_s_timed_region": round(wall, 3),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic(w.name, "proj"),
+            "kernel": f"proj_bf16_kernel<{str(w.tangent).lower()}>",
+            "avg_launch_ms": round(avg_launch_ms, 4),
+            "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4),
+            "min_launch_ms": round(launch_ms[0], 4),
+            "algorithmic_flops_per_launch": w.flops,
+            "algorithmic_bytes_per_launch": w.algorithmic_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the fp64 oracle on a block of tokens (cpu_baseline)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_proj(w, proj_host_inputs(w), args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +240,8 @@ def main():
     ap.add_argument("--frozen-context", action="store_true",
                     help="pass tk = tv = NULL (workloads whose key tangents are zero); "
                          "value is then executed TFLOP/s at 8 flops per logit and head dim")
+    ap.add_argument("--proj", default=None,
+                    help="time the projection into attention heads (attn_jvp_proj) on this projection workload")
     args = ap.parse_args()
 
     if args.split and not 1 <= args.split <= 16:
@@ -132,6 +252,16 @@ def main():
               "(the attention JVP shards by (batch, head) with no exchange: run one process per GPU)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.proj is not None:
+        from workloads import PROJ_WORKLOADS
+
+        if args.proj not in PROJ_WORKLOADS or args.split or args.frozen_context:
+            print(f"bench.py: --proj takes one of {sorted(PROJ_WORKLOADS)} (without --split or --frozen-context)",
+                  file=sys.stderr)
+            sys.exit(2)
+        bench_proj(args)
+        return
 
     import torch
 

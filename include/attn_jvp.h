@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define ATTN_JVP_VERSION 10100 /* 1.1.0 */
+#define ATTN_JVP_VERSION 10200 /* 1.2.0 */
 
 /* Largest number of partial results one attn_jvp_merge call combines. */
 #define ATTN_JVP_MAX_MERGE_PARTS 16
@@ -159,6 +159,50 @@ int attn_jvp_merge(int n, const void* const* o_parts, const void* const* to_part
                    const float* const* lse_parts, const float* const* tlse_parts,
                    void* o, void* to, float* lse, float* tlse,
                    int64_t rows, int64_t d, int dtype, void* stream);
+
+/*
+ * attn_jvp_proj — the projection of hidden states into attention heads, with
+ * its tangent: the layer that hands Q, K, V and their tangents to attn_jvp_fwd.
+ *
+ * The rCM pages refactor every layer of the distilled networks to take and
+ * return tangents, and distribute the tangents of Q, K and V like Q, K and V
+ * (ai.info summary of "Large Scale Diffusion Distillation via Score-Regularized
+ * Continuous-Time Consistency", "Methodology in Plain English" and "Key
+ * Contributions" item 1).  They name no architecture; this is the plain
+ * reading, a linear layer with bias whose JVP is its linear part applied to
+ * the tangent (a constant bias has no tangent):
+ *
+ *   Y  = X W^T + b          TY = TX W^T
+ *
+ * with output feature f = (n*H + h)*d + j of token t of batch b written to
+ * element [n, b, h, t, j]: projection n (Q, K, V in that order for n_out = 3),
+ * head h, in the [B, H, L, d] layout attn_jvp_fwd reads.  One pass computes
+ * both products from the same weight tiles.
+ *
+ * Arguments
+ *   x, tx  [B, L, D]            hidden states and their tangent (device, read only).
+ *                               tx and ty may both be NULL: a frozen input (the text
+ *                               context of a cross-attention), no tangent computed
+ *   w      [n_out*H*d, D]       weight, row f holds output feature f (the layout of a
+ *                               linear layer's weight)                  (device, read only)
+ *   bias   [n_out*H*d] or NULL  added to Y only                         (device, read only)
+ *   y, ty  [n_out, B, H, L, d]  outputs; projection n of the batch starts
+ *                               n*B*H*L*d elements after the pointer     (device, written)
+ *   B, L, D, n_out, H, d        sizes; d in {64, 128}; D a positive multiple of 64
+ *   dtype                       ATTN_JVP_BF16 (bf16 products, float32 accumulation,
+ *                               outputs rounded to nearest even); ATTN_JVP_FP32 is
+ *                               ATTN_JVP_EUNSUPPORTED
+ *   stream                      as attn_jvp_fwd
+ *
+ * Layout, ownership, alignment (16 bytes for every pointer), execution and
+ * errors follow attn_jvp_fwd.  Exactly one of tx, ty NULL is ATTN_JVP_EINVAL;
+ * B*L == 0 or n_out*H == 0 is a no-op.  Limits: L*D, n_out*H*d*D and L*d below
+ * 2^31 elements, D below 2^22.  Outputs must not overlap any input.
+ */
+int attn_jvp_proj(const void* x, const void* tx, const void* w, const void* bias,
+                  void* y, void* ty,
+                  int64_t B, int64_t L, int64_t D, int64_t n_out, int64_t H, int64_t d,
+                  int dtype, void* stream);
 
 /* Static description of a status code ("unknown status" for others). */
 const char* attn_jvp_status_string(int status);

@@ -31,13 +31,13 @@ def declared_functions():
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == ["attn_jvp_fwd", "attn_jvp_fwd_part", "attn_jvp_last_error", "attn_jvp_merge",
-                     "attn_jvp_status_string", "attn_jvp_version"]
+                     "attn_jvp_proj", "attn_jvp_status_string", "attn_jvp_version"]
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert A.attn_jvp_version() == 10100
+    assert A.attn_jvp_version() == 10200
     assert A.attn_jvp_status_string(0) == "ok"
     assert A.attn_jvp_status_string(A.ATTN_JVP_EUNSUPPORTED).startswith("unsupported")
     assert A.attn_jvp_status_string(99) == "unknown status"
@@ -131,6 +131,7 @@ def test_ctypes_signature_is_c_abi(lib):
     assert len(lib.attn_jvp_fwd.argtypes) == 17
     assert len(lib.attn_jvp_fwd_part.argtypes) == 19
     assert len(lib.attn_jvp_merge.argtypes) == 13
+    assert len(lib.attn_jvp_proj.argtypes) == 14
 
 
 def test_merge_part_limit_matches_header():
@@ -191,3 +192,44 @@ def test_new_entry_points_report_launch_error_without_device(lib):
         pytest.skip("a GPU is present: this checks the no-device path only")
     assert call_part() == A.ATTN_JVP_ELAUNCH
     assert call_merge() == A.ATTN_JVP_ELAUNCH
+
+
+def call_proj(ptrs=None, B=1, L=8, D=64, n_out=3, H=2, d=64, dtype=1):
+    p = ptrs if ptrs is not None else [FAKE] * 6
+    return A.attn_jvp_proj(*p, B, L, D, n_out, H, d, dtype)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), A.ATTN_JVP_EINVAL),
+    (dict(dtype=0), A.ATTN_JVP_EUNSUPPORTED),
+    (dict(L=-1), A.ATTN_JVP_EINVAL),
+    (dict(D=-64), A.ATTN_JVP_EINVAL),
+    (dict(d=32), A.ATTN_JVP_EUNSUPPORTED),
+    (dict(D=96), A.ATTN_JVP_EUNSUPPORTED),
+    (dict(D=0), A.ATTN_JVP_EUNSUPPORTED),
+    (dict(ptrs=[0] + [FAKE] * 5), A.ATTN_JVP_EINVAL),
+    (dict(ptrs=[FAKE] * 4 + [0, FAKE]), A.ATTN_JVP_EINVAL),
+    (dict(ptrs=[FAKE, 0] + [FAKE] * 4), A.ATTN_JVP_EINVAL),
+    (dict(ptrs=[FAKE] * 5 + [0]), A.ATTN_JVP_EINVAL),
+    (dict(ptrs=[FAKE, FAKE + 8] + [FAKE] * 4), A.ATTN_JVP_EALIGN),
+    (dict(ptrs=[FAKE] * 3 + [FAKE + 2] + [FAKE] * 2), A.ATTN_JVP_EALIGN),
+    (dict(L=1 << 20, D=1 << 12), A.ATTN_JVP_EUNSUPPORTED),
+    (dict(D=1 << 22, L=1), A.ATTN_JVP_EUNSUPPORTED),
+])
+def test_proj_rejects_invalid_arguments(lib, kw, status):
+    assert call_proj(**kw) == status
+    assert A.attn_jvp_last_error() != ""
+
+
+def test_proj_zero_size_is_ok_without_pointers(lib):
+    for kw in (dict(B=0), dict(L=0), dict(n_out=0), dict(H=0)):
+        assert call_proj(ptrs=[0] * 6, **kw) == A.ATTN_JVP_OK
+
+
+def test_proj_without_tangent_or_bias_passes_host_checks(lib):
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this checks the no-device path only")
+    assert call_proj(ptrs=[FAKE, 0, FAKE, 0, FAKE, 0]) == A.ATTN_JVP_ELAUNCH
+    assert call_proj() == A.ATTN_JVP_ELAUNCH

@@ -28,3 +28,11 @@ def test_split_part_count_is_checked():
     r = bench("--split", "17")
     assert r.returncode == 2
     assert "--split" in r.stderr
+
+
+def test_projection_workload_is_checked():
+    r = bench("--proj", "no_such_projection")
+    assert r.returncode == 2
+    assert "qkv_video_bf16" in r.stderr
+    r = bench("--proj", "qkv_video_bf16", "--split", "2")
+    assert r.returncode == 2
