@@ -21,12 +21,13 @@
 //    (W | X | TX tiles, 64 KB per stage) by buffer_load ... lds, rows of 128
 //    bytes with XOR-swizzled 16-byte units; each W fragment read from LDS
 //    feeds two MFMAs (X and TX);
-//  * software pipeline per step: fenced units of one MFMA each, the next
-//    step's copies issued in the first units and the fragment reads a few units
-//    ahead of their use.  The barrier that publishes the next step's tiles sits
-//    near the end of the step, after the last read of the current stage, so
-//    the next step's first fragments are read before the step ends and no step
-//    starts by waiting on LDS;
+//  * software pipeline per step: fenced units of one MFMA each, fragment reads
+//    16 units ahead of their use.  The barrier that publishes the next step's
+//    tiles sits three quarters into the step, after the last read of the
+//    current stage, so the next step's first fragments are read before the
+//    step ends (no step starts by waiting on LDS), and most copies of the step
+//    after next are issued right behind it, into the stage just released, a
+//    whole step ahead of the barrier that waits for them;
 //  * the bias initialises the X accumulators; the epilogue rounds to bf16 and
 //    stores 16 bytes per lane after pairing the half-waves with v_permlane32_swap.
 //  * kTangent = false (a frozen input, no TX): X tiles and accumulators only.
@@ -44,8 +45,8 @@ constexpr int kWTile = kTF * kRowB;            // 32 KB
 constexpr int kXTile = kTT * kRowB;            // 16 KB
 constexpr int kStageB = kWTile + 2 * kXTile;   // W | X | TX
 constexpr int kFB = kTF / 32;                  // 32-feature blocks per tile
-constexpr int kGroupF = 8;                     // feature tiles per dispatch group
-constexpr int kRing = 8;                       // W fragment registers in flight
+constexpr int kGroupF = 16;                    // feature tiles per dispatch group
+constexpr int kRing = 16;                      // W fragment registers in flight
 
 struct ProjParams {
   const void* x;
@@ -77,29 +78,47 @@ __device__ inline uint32_t slice_voff(int s, int lane, int D) {
 }
 
 // Schedule of one step (see the file comment).  W fragment q = 8c + fb (hidden
-// chunk c of 16, feature block fb) is used by units q*kPer .. q*kPer + kPer - 1.
+// chunk c of 16, feature block fb) is used by units q*kPer .. q*kPer + kPer - 1
+// and lives in register slot q % kRing; X fragment c in slot c % 2.  Step k
+// computes on stage k & 1.  Its copies are issued in two parts: kTail slices
+// of step k + 2 right after step k's barrier (from then on no wave reads stage
+// k & 1), and the other slices of step k + 1 in the first units of step k, one
+// every second unit.  The barrier at unit kBar waits for all of them.
 template <bool kT>
 struct Sched {
   static constexpr int kPer = kT ? 2 : 1;                   // MFMAs per W fragment
   static constexpr int kUnits = 32 * kPer;                  // MFMAs per step and wave
-  static constexpr int kLead = kT ? 8 : 5;                  // W read this many units before use
+  static constexpr int kLead = kT ? 16 : 5;                 // W read this many units before use
   static constexpr int kPre = (kLead + kPer - 1) / kPer;    // W fragments read in the previous step
-  static constexpr int kXLead = kT ? 10 : 7;                // X read units before chunk c starts
-  static constexpr int kBar = kT ? 56 : 27;                 // unit of the mid-step barrier
+  static constexpr int kXLead = kT ? 16 : 7;                // X read units before chunk c starts
+  static constexpr int kBar = kT ? 48 : 27;                 // unit of the mid-step barrier
   static constexpr int kNX = kT ? 2 : 1;                    // X fragments per chunk (X, TX)
   static constexpr int kDma = ((kWTile + kNX * kXTile) / 1024) / kWaves;  // slices per wave
   static constexpr int kWDma = kWTile / 1024 / kWaves;                    // of which W
-  static_assert(31 * kPer - kLead < kBar, "current-stage W reads end before the barrier");
-  static_assert(3 * 8 * kPer - kXLead + kNX - 1 < kBar, "current-stage X reads end before the barrier");
-  static_assert(kDma <= kBar, "copies issued before the barrier");
+  static constexpr int kTail = kT ? 12 : 4;                 // slices of step k + 2 after the barrier
+  static constexpr int kHeadStride = kT ? 2 : 1;            // units between head copies
   // unit of the i-th next-stage read (X fragments first, then W 0 .. kPre - 1);
   // reads that do not fit go to the last unit
   static constexpr int next_unit(int i) { return kBar + i < kUnits ? kBar + i : kUnits - 1; }
-  // every next-stage W fragment is read at least 4 units before its first use
+  // a next-stage W fragment goes into a slot whose current fragment is done
+  static constexpr bool next_w_slots_free() {
+    for (int q2 = 0; q2 < kPre; ++q2)
+      for (int q = q2 % kRing; q < 32; q += kRing)
+        if ((q + 1) * kPer - 1 >= next_unit(kNX + q2)) return false;
+    return true;
+  }
+  static_assert(31 * kPer - kLead < kBar, "current-stage W reads end before the barrier");
+  static_assert(3 * 8 * kPer - kXLead + kNX - 1 < kBar, "current-stage X reads end before the barrier");
+  static_assert(kLead <= (kRing - 1) * kPer, "a W read does not overwrite a fragment still in use");
+  static_assert(kXLead <= 8 * kPer, "an X read does not overwrite a chunk still in use");
+  static_assert(kBar >= 24 * kPer, "next-stage X chunk 0 (slot 0) is read after chunk 2's last use");
+  static_assert(next_w_slots_free(), "next-stage W reads do not overwrite fragments still in use");
+  static_assert((kDma - kTail - 1) * kHeadStride < kBar, "head copies issued before the barrier");
+  static_assert(kBar + kTail <= kUnits, "tail copies fit after the barrier");
+  // every next-stage fragment is read at least 4 units before its first use
   static_assert(kUnits - next_unit(kNX + kPre - 1) + (kPre - 1) * kPer >= 4, "next-stage lead");
   static_assert(kUnits - next_unit(kNX) >= 4, "next-stage lead of W fragment 0");
 };
-
 template <bool kT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void proj_bf16_kernel(ProjParams p) {
@@ -192,16 +211,19 @@ void proj_bf16_kernel(ProjParams p) {
   };
 
   // One step: MFMAs on stage k & 1; with kMore, the copies of step k + 1, the
-  // barrier that publishes them, and the first reads of step k + 1.
-  auto step = [&](int k, auto more) {
+  // barrier that publishes them and the first reads of step k + 1; with kMore2,
+  // the tail copies of step k + 2.
+  auto step = [&](int k, auto more, auto more2) {
     constexpr bool kMore = decltype(more)::value;
+    constexpr bool kMore2 = decltype(more2)::value;
     const char* cur = smem + (k & 1) * kStageB;
     const char* nxt = smem + ((k + 1) & 1) * kStageB;
     static_for<0, S::kUnits>([&](auto iu) {
       constexpr int u = decltype(iu)::value;
       constexpr int q = u / S::kPer, c = q / 8, fb = q % 8, which = u % S::kPer;
       acc[which][fb] = mfma(wf[q % kRing], xf[c & 1][which], acc[which][fb]);
-      if constexpr (kMore && u < S::kDma) issue(k + 1, IC<u>{});
+      if constexpr (kMore && u % S::kHeadStride == 0 && u / S::kHeadStride < S::kDma - S::kTail)
+        issue(k + 1, IC<S::kTail + u / S::kHeadStride>{});
       // current stage: W fragment q2 read kLead units before its first use
       static_for<S::kPre, 32>([&](auto iq) {
         constexpr int q2 = decltype(iq)::value;
@@ -227,6 +249,7 @@ void proj_bf16_kernel(ProjParams p) {
           constexpr int q2 = decltype(iq)::value;
           if constexpr (S::next_unit(S::kNX + q2) == u) read_w(nxt, iq);
         });
+        if constexpr (kMore2 && u >= S::kBar && u < S::kBar + S::kTail) issue(k + 2, IC<u - S::kBar>{});
       }
       fence();
     });
@@ -238,9 +261,11 @@ void proj_bf16_kernel(ProjParams p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   static_for<0, S::kNX>([&](auto iw) { read_x(smem, IC<0>{}, iw); });
+  if (nk > 1) static_for<0, S::kTail>([&](auto ii) { issue(1, ii); });  // step 1's tail slices: stage 1 is free
   static_for<0, S::kPre>([&](auto iq) { read_w(smem, iq); });
-  for (int k = 0; k < nk - 1; ++k) step(k, std::true_type{});
-  step(nk - 1, std::false_type{});
+  for (int k = 0; k < nk - 2; ++k) step(k, std::true_type{}, std::true_type{});
+  if (nk > 1) step(nk - 2, std::true_type{}, std::false_type{});
+  step(nk - 1, std::false_type{}, std::false_type{});
 
   // ---- epilogue ----------------------------------------------------------------
   // Accumulator group g (registers 4g .. 4g + 3) of a lane holds features
