@@ -86,3 +86,40 @@ def test_split_and_merge_replay_in_a_graph(A):
         torch.cuda.synchronize()
         for got, want in zip(out, ref):
             assert torch.equal(got, want), i
+
+
+def test_projection_then_attention_replays_in_a_graph(A):
+    """The projection with its tangent followed by the attention JVP on its
+    outputs: one captured layer pass, replayed against the eager result."""
+    from workloads import custom_proj
+    from workloads.device import device_proj_inputs
+
+    w = custom_proj(1, 190, 256, 3, 2, 128, seed_id=7200)
+    print("case graph projection + attention", flush=True)
+    x = device_proj_inputs(w)
+    y, ty = A.proj(x["x"], x["tx"], x["w"], x["bias"], n_out=3, heads=2)
+    ref = [y.clone(), ty.clone()] + [t.clone() for t in A.fwd(y[0], y[1], y[2], ty[0], ty[1], ty[2])]
+    ys = (torch.empty_like(y), torch.empty_like(ty))
+    att = tuple(torch.empty_like(t) for t in ref[2:])
+
+    def body():
+        A.proj(x["x"], x["tx"], x["w"], x["bias"], n_out=3, heads=2, out=ys)
+        A.fwd(ys[0][0], ys[0][1], ys[0][2], ys[1][0], ys[1][1], ys[1][2], out=att)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        body()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    for i in range(4):
+        for t in ys + att:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(ys + att, ref):
+            assert torch.equal(got, want), i
