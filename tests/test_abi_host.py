@@ -233,3 +233,10 @@ def test_proj_without_tangent_or_bias_passes_host_checks(lib):
         pytest.skip("a GPU is present: this checks the no-device path only")
     assert call_proj(ptrs=[FAKE, 0, FAKE, 0, FAKE, 0]) == A.ATTN_JVP_ELAUNCH
     assert call_proj() == A.ATTN_JVP_ELAUNCH
+
+
+def test_sizes_one_past_the_stated_limits_are_rejected(lib):
+    n = (1 << 29) // 128  # Lq*d or Lk*d = 2^29
+    assert A.attn_jvp_fwd(*([FAKE] * 9), 1, 1, n, 8, 128, 0.1, 1) == A.ATTN_JVP_EUNSUPPORTED
+    assert A.attn_jvp_fwd(*([FAKE] * 9), 1, 1, 8, n, 128, 0.1, 1) == A.ATTN_JVP_EUNSUPPORTED
+    assert A.attn_jvp_proj(*([FAKE] * 6), 1, 1 << 18, 8192, 1, 2, 128, 1) == A.ATTN_JVP_EUNSUPPORTED  # L*D = 2^31
