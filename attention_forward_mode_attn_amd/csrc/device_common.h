@@ -130,6 +130,16 @@ __device__ inline float xhalf_sum(float x) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Pair accumulator groups g (in x) and g + 1 (in y) of one lane across the two
+// half-waves with v_permlane32_swap: a lane of half 0 ends up with the 8
+// consecutive rows of group g (its own 4 and its partner's 4), a lane of half
+// 1 with those of group g + 1, as one 16-byte store of packed bf16 pairs.
+__device__ inline u32x4 pair_halves(u32x2 x, u32x2 y) {
+  const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
+  return u32x4{s0[0], s1[0], s0[1], s1[1]};
+}
+
 // Key offset (within a 32-key block) held by accumulator register r of half hh.
 __device__ inline int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 

@@ -561,11 +561,6 @@ void attn_jvp_bf16_kernel(Params p) {
   // first store: reusing a store's data registers right after it makes the
   // next write wait until the queued store has read them.
   u32x4 ost[C::kBlocksD][2], tst[C::kBlocksD][2];
-  auto pair = [](u32x2 x, u32x2 y) {  // x: group g, y: group g + 1 of this lane
-    const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
-    return u32x4{s0[0], s1[0], s0[1], s1[1]};
-  };
 #pragma unroll
   for (int b = 0; b < C::kBlocksD; ++b) {
 #pragma unroll
@@ -584,8 +579,8 @@ void attn_jvp_bf16_kernel(Params p) {
         op[h] = u32x2{pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3])};
         tp[h] = u32x2{pack_bf16(tv4[0], tv4[1]), pack_bf16(tv4[2], tv4[3])};
       }
-      ost[b][gp] = pair(op[0], op[1]);
-      tst[b][gp] = pair(tp[0], tp[1]);
+      ost[b][gp] = pair_halves(op[0], op[1]);
+      tst[b][gp] = pair_halves(tp[0], tp[1]);
     }
   }
   fence();

@@ -30,7 +30,7 @@
 //    whole step ahead of the barrier that waits for them;
 //  * the bias initialises the X accumulators; the epilogue rounds to bf16 and
 //    stores 16 bytes per lane after pairing the half-waves with v_permlane32_swap.
-//  * kTangent = false (a frozen input, no TX): X tiles and accumulators only.
+//  * kT = false (a frozen input, no TX): X tiles and accumulators only.
 #include "device_common.h"
 #include "launch.h"
 
@@ -273,11 +273,6 @@ void proj_bf16_kernel(ProjParams p) {
   // half-waves so that each lane holds 8 consecutive features (half 0:
   // 16gp .. +7, half 1: 16gp + 8 .. +15), one 16-byte store each.  Everything is
   // packed before the first store.
-  auto pair = [](u32x2 x, u32x2 y) {
-    const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
-    return u32x4{s0[0], s1[0], s0[1], s1[1]};
-  };
   u32x4 pk[S::kNX][kFB][2];
 #pragma unroll
   for (int w2 = 0; w2 < S::kNX; ++w2)
@@ -292,7 +287,7 @@ void proj_bf16_kernel(ProjParams p) {
           h2[h] = u32x2{pack_bf16(acc[w2][fb][4 * g], acc[w2][fb][4 * g + 1]),
                         pack_bf16(acc[w2][fb][4 * g + 2], acc[w2][fb][4 * g + 3])};
         }
-        pk[w2][fb][gp] = pair(h2[0], h2[1]);
+        pk[w2][fb][gp] = pair_halves(h2[0], h2[1]);
       }
   fence();
   const int token = t0 + wv * 32 + n;  // rows at or past L fall outside the output range: dropped
