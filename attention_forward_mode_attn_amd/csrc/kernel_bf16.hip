@@ -137,6 +137,9 @@ void attn_jvp_bf16_kernel(Params p) {
   const int t = threadIdx.x;
   const int lane = t & 63, n = lane & 31, hh = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  // All kernel arguments in scalar registers before the first is used: one
+  // round trip to the argument buffer instead of one per use site.
+  asm volatile("" : : "s"(p.q), "s"(p.k), "s"(p.v), "s"(p.tq), "s"(p.tk), "s"(p.tv), "s"(p.n_blocks));
   const int blk = xcd_logical_block(blockIdx.x, p.n_blocks);
   const int bh = blk / p.n_qtiles, qt = blk % p.n_qtiles;
   const int Lq = p.Lq, Lk = p.Lk;
@@ -415,10 +418,16 @@ void attn_jvp_bf16_kernel(Params p) {
   float my;  // row max of y over the tile waiting in (yv, tsv)
 
   // ---- prologue: tile 0 logits; its max sets the exponent base --------------
+  // The tile-0 logits need Q and K|tK of tile 0 only: the later copies (V|tV
+  // of tile 0, K|tK of tile 1) keep landing under them.  Vector memory
+  // operations complete in order, so vmcnt(kLater) leaves exactly those in
+  // flight.
   issue(0, 0);
   issue(0, 2);
   issue(1, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): all DMA of this wave landed
+  constexpr int kLater = 2 * (kFrozen ? 1 : 2) * C::kLoadsPerWave;
+  static_assert(kLater < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (kLater & 15) | ((kLater >> 4) << 14));  // vmcnt(kLater)
   __syncthreads();
   {
     f32x16 sn[2], tsn[2];
@@ -433,7 +442,8 @@ void attn_jvp_bf16_kernel(Params p) {
     Take tk;
     all_steps(IC<0>{}, IC<64>{}, IC<2>{}, [&](auto is, auto ix) { take_step(is, ix, tk, sn, tsn); });
   }
-  __syncthreads();  // every wave is done with K of tile 0 before it is refilled
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): V|tV of tile 0 and K|tK of tile 1 landed
+  __syncthreads();  // ... for every wave, and every wave is done with K of tile 0 before it is refilled
 
   // ---- one pipelined iteration ------------------------------------------------
   // Phase A: the 48 logit MFMAs of tile j + 1, each paired with softmax
