@@ -67,6 +67,52 @@ def measured_traffic(workload: str, kernel: str = "attention"):
     return float(m_b.group(1))
 
 
+def sclk_path(torch):
+    """The sysfs `pp_dpm_sclk` file of the card that torch's device 0 is on
+    (matched by PCI domain and bus), or None where there is none."""
+    import glob
+
+    props = torch.cuda.get_device_properties(0)
+    bus, dom = getattr(props, "pci_bus_id", None), getattr(props, "pci_domain_id", 0)
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        try:
+            uevent = open(os.path.join(dev, "uevent")).read()
+        except OSError:
+            continue
+        m = re.search(r"PCI_SLOT_NAME=([0-9a-fA-F]+):([0-9a-fA-F]+):", uevent)
+        path = os.path.join(dev, "pp_dpm_sclk")
+        if m and bus is not None and int(m.group(2), 16) == bus and int(m.group(1), 16) == dom \
+                and os.path.exists(path):
+            return path
+    return None
+
+
+def read_sclk_mhz(path):
+    """The current shader clock: the entry marked '*' in pp_dpm_sclk."""
+    try:
+        m = re.search(r"(\d+)\s*Mhz\s*\*", open(path).read(), re.I)
+    except OSError:
+        return None
+    return int(m.group(1)) if m else None
+
+
+def wait_sampling_sclk(path, done, period_s: float = 0.01):
+    """Wait for the event `done` while sampling the shader clock; returns the
+    sclk summary for the JSON line (None without samples)."""
+    samples = []
+    while not done.query():
+        if path:
+            v = read_sclk_mhz(path)
+            if v:
+                samples.append(v)
+        time.sleep(period_s)
+    if not samples:
+        return None
+    samples.sort()
+    return {"median": samples[len(samples) // 2], "min": samples[0], "max": samples[-1],
+            "samples": len(samples), "source": "pp_dpm_sclk, sampled while the timed launches ran"}
+
+
 def _blas_cores() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -179,6 +225,7 @@ def bench_proj(args):
         step()
         b.record(stream)
     ev1.record(stream)
+    sclk = wait_sampling_sclk(sclk_path(torch), ev1)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
@@ -203,6 +250,7 @@ def bench_proj(args):
                    "tangent": w.tangent, "bias": w.bias, "parallelism": "single GPU"},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "wall_s_timed_region": round(wall, 3),
+        "sclk_mhz": sclk,
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
@@ -333,6 +381,7 @@ def main():
         step()
         b.record(stream)
     ev1.record(stream)
+    sclk = wait_sampling_sclk(sclk_path(torch), ev1)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = ev0.elapsed_time(ev1)
@@ -403,6 +452,7 @@ def main():
                    + (f"; {args.split} key shards + exact merge" if args.split else "")},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "wall_s_timed_region": round(wall, 3),
+        "sclk_mhz": sclk,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

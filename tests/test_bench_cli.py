@@ -36,3 +36,34 @@ def test_projection_workload_is_checked():
     assert "qkv_video_bf16" in r.stderr
     r = bench("--proj", "qkv_video_bf16", "--split", "2")
     assert r.returncode == 2
+
+
+def test_sclk_parsing_and_sampling(tmp_path):
+    """The shader clock is the entry marked '*' of pp_dpm_sclk, in either of its
+    layouts (a separate current-clock line, or a marked level); the sampler
+    summarises what it read while the event was pending."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("S: 1843Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
+    assert bench.read_sclk_mhz(str(f)) == 1843
+    f.write_text("0: 500Mhz\n1: 1500Mhz *\n2: 2100Mhz\n")
+    assert bench.read_sclk_mhz(str(f)) == 1500
+    f.write_text("0: 500Mhz\n1: 2400Mhz\n")
+    assert bench.read_sclk_mhz(str(f)) is None
+    assert bench.read_sclk_mhz(str(tmp_path / "missing")) is None
+
+    class Pending:
+        def __init__(self, n):
+            self.n = n
+
+        def query(self):
+            self.n -= 1
+            return self.n < 0
+
+    f.write_text("S: 1700Mhz *\n")
+    s = bench.wait_sampling_sclk(str(f), Pending(3), period_s=0.0)
+    assert s["samples"] == 3 and s["median"] == s["min"] == s["max"] == 1700
+    assert bench.wait_sampling_sclk(None, Pending(3), period_s=0.0) is None
+    assert bench.wait_sampling_sclk(str(f), Pending(0), period_s=0.0) is None
