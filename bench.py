@@ -96,9 +96,11 @@ def read_sclk_mhz(path):
     return int(m.group(1)) if m else None
 
 
-def wait_sampling_sclk(path, done, period_s: float = 0.01):
+def wait_sampling_sclk(path, done, period_s: float = 0.01, min_samples: int = 20):
     """Wait for the event `done` while sampling the shader clock; returns the
-    sclk summary for the JSON line (None without samples)."""
+    sclk summary for the JSON line.  None with fewer than `min_samples` samples:
+    the firmware's figure trails the load, so a timed region much shorter than
+    0.2 s does not show the clock it ran at."""
     samples = []
     while not done.query():
         if path:
@@ -106,7 +108,7 @@ def wait_sampling_sclk(path, done, period_s: float = 0.01):
             if v:
                 samples.append(v)
         time.sleep(period_s)
-    if not samples:
+    if len(samples) < min_samples:
         return None
     samples.sort()
     return {"median": samples[len(samples) // 2], "min": samples[0], "max": samples[-1],

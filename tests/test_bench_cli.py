@@ -63,7 +63,8 @@ def test_sclk_parsing_and_sampling(tmp_path):
             return self.n < 0
 
     f.write_text("S: 1700Mhz *\n")
-    s = bench.wait_sampling_sclk(str(f), Pending(3), period_s=0.0)
+    s = bench.wait_sampling_sclk(str(f), Pending(3), period_s=0.0, min_samples=3)
     assert s["samples"] == 3 and s["median"] == s["min"] == s["max"] == 1700
+    assert bench.wait_sampling_sclk(str(f), Pending(2), period_s=0.0, min_samples=3) is None  # too short a run
     assert bench.wait_sampling_sclk(None, Pending(3), period_s=0.0) is None
     assert bench.wait_sampling_sclk(str(f), Pending(0), period_s=0.0) is None

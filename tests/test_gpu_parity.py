@@ -85,6 +85,13 @@ def test_image_self_bf16(A):
     check(w, compare(w, o, to, lse), per_head_gate=True)
 
 
+def test_image_self_fp32_sampled(A):
+    w = WORKLOADS["image_self_fp32"]
+    print(f"case {w.name} (256 sampled rows per head)", flush=True)
+    _, o, to, lse = run(A, w)
+    check(w, compare(w, o, to, lse, rows_fn=lambda b, h: sample_rows(w, b, h)), per_head_gate=True)
+
+
 def test_text_cross_bf16(A):
     w = WORKLOADS["text_cross_bf16"]
     print(f"case {w.name} (all rows)", flush=True)

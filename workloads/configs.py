@@ -81,6 +81,11 @@ WORKLOADS = {
             description="image-token self-attention JVP (64x64 latent patches)",
         ),
         Workload(
+            "image_self_fp32", 6, B=2, H=16, Lq=4096, Lk=4096, d=128, dtype="fp32",
+            std=_std(tq=0.5, tk=0.5, tv=0.5),
+            description="the image-token self-attention JVP in fp32 in/out/compute",
+        ),
+        Workload(
             "text_cross_bf16", 3, B=2, H=16, Lq=4096, Lk=512, d=128, dtype="bf16",
             std=_std(tk=0.0, tv=0.0),
             description="image queries x text keys, frozen text context (tK = tV = 0)",
