@@ -63,7 +63,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* tq, const 
     if (!aligned(x, 16)) return fail(ATTN_JVP_EALIGN, "tensor pointers must be 16-byte aligned");
   if (!aligned(lse, 4) || !aligned(tlse, 4)) return fail(ATTN_JVP_EALIGN, "lse and tlse must be 4-byte aligned");
   const int64_t lim = int64_t(1) << 29;  // elements per head: keeps byte offsets within 32 bits
-  if (Lq * d >= lim || Lk * d >= lim) return fail(ATTN_JVP_EUNSUPPORTED, "sequence too long for one head");
+  if (Lq >= lim / d || Lk >= lim / d) return fail(ATTN_JVP_EUNSUPPORTED, "sequence too long for one head");
   if (kv_rows > INT32_MAX) return fail(ATTN_JVP_EUNSUPPORTED, "kv_rows too large");
   const int64_t qtiles = (Lq + 127) / 128;
   if (B > INT32_MAX || H > INT32_MAX || B * H > INT32_MAX || B * H * qtiles >= (int64_t(1) << 31))
@@ -157,12 +157,16 @@ int attn_jvp_proj(const void* x, const void* tx, const void* w, const void* bias
   const void* p16[] = {x, tx, w, bias, y, ty};
   for (const void* q : p16)
     if (!aligned(q, 16)) return fail(ATTN_JVP_EALIGN, "pointers must be 16-byte aligned");
+  // Every factor is bounded before it is multiplied, so no product below can
+  // overflow 64 bits whatever the caller passes.
   const int64_t lim = int64_t(1) << 31;
+  if (B >= lim || L >= lim || n_out >= lim || H >= lim || D >= (int64_t(1) << 22) || n_out * H >= lim)
+    return fail(ATTN_JVP_EUNSUPPORTED, "size beyond the projection's limits");
   const int64_t F = n_out * H * d;
-  if (n_out >= lim || H >= lim || F >= lim || L * D >= lim || F * D >= lim || L * d >= lim || D >= (int64_t(1) << 22))
+  if (F >= lim || L * D >= lim || F * D >= lim || L * d >= lim)
     return fail(ATTN_JVP_EUNSUPPORTED, "size beyond the projection's limits");
   const int64_t blocks = ((F + 255) / 256) * ((L + 127) / 128) * B;
-  if (B >= lim || blocks >= lim) return fail(ATTN_JVP_EUNSUPPORTED, "too many workgroups");
+  if (blocks >= lim) return fail(ATTN_JVP_EUNSUPPORTED, "too many workgroups");
   attnjvp::ProjProblem p;
   p.x = x; p.tx = tx; p.w = w; p.bias = bias; p.y = y; p.ty = ty;
   p.B = (int)B; p.L = (int)L; p.D = (int)D; p.n_out = (int)n_out; p.H = (int)H; p.d = (int)d;

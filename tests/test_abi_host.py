@@ -240,3 +240,15 @@ def test_sizes_one_past_the_stated_limits_are_rejected(lib):
     assert A.attn_jvp_fwd(*([FAKE] * 9), 1, 1, n, 8, 128, 0.1, 1) == A.ATTN_JVP_EUNSUPPORTED
     assert A.attn_jvp_fwd(*([FAKE] * 9), 1, 1, 8, n, 128, 0.1, 1) == A.ATTN_JVP_EUNSUPPORTED
     assert A.attn_jvp_proj(*([FAKE] * 6), 1, 1 << 18, 8192, 1, 2, 128, 1) == A.ATTN_JVP_EUNSUPPORTED  # L*D = 2^31
+
+
+def test_absurd_sizes_are_rejected_without_overflow(lib):
+    """Sizes whose products overflow 64 bits are rejected as unsupported (every
+    factor is bounded before it is multiplied)."""
+    big = (1 << 62) + 3
+    assert A.attn_jvp_fwd(*([FAKE] * 9), 1, 1, big, 8, 128, 0.1, 1) == A.ATTN_JVP_EUNSUPPORTED
+    assert A.attn_jvp_fwd(*([FAKE] * 9), 1, 1, 8, big, 64, 0.1, 0) == A.ATTN_JVP_EUNSUPPORTED
+    assert A.attn_jvp_fwd(*([FAKE] * 9), big, big, 8, 8, 128, 0.1, 1) == A.ATTN_JVP_EUNSUPPORTED
+    for kw in (dict(n_out=1 << 40, H=1 << 40), dict(L=big), dict(B=big), dict(D=big - 3),
+               dict(n_out=(1 << 31) - 1, H=(1 << 31) - 1)):
+        assert call_proj(**kw) == A.ATTN_JVP_EUNSUPPORTED, kw
