@@ -159,11 +159,23 @@ def fwd(q, k, v, tq, tk, tv, scale=None, out=None, stream=None):
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
     else:
         o, to, lse = out
+        _check_out(o, q.shape, q.dtype, q.device, "o")
+        _check_out(to, q.shape, q.dtype, q.device, "to")
+        _check_out(lse, (B, H, Lq), torch.float32, q.device, "lse")
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     status = attn_jvp_fwd(q, k, v, tq, tk, tv, o, to, lse, B, H, Lq, Lk, d, scale, dtype, s.cuda_stream)
     if status != ATTN_JVP_OK:
         raise AttnJvpError(status, attn_jvp_last_error())
     return o, to, lse
+
+
+def _check_out(x, shape, dtype, device, what):
+    """An output buffer passed by the caller: exactly the shape, dtype and
+    device the kernel writes, contiguous (the kernels write every element of
+    that extent and nothing else)."""
+    if x is None or tuple(x.shape) != tuple(shape) or x.dtype != dtype or x.device != device \
+            or not x.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous {dtype} tensor of shape {tuple(shape)} on {device}")
 
 
 def _check_inputs(q, k, v, tq, tk, tv):
@@ -172,6 +184,8 @@ def _check_inputs(q, k, v, tq, tk, tv):
     dt = q.dtype
     if dt not in (torch.float32, torch.bfloat16):
         raise TypeError("q must be float32 or bfloat16")
+    if q.device.type != "cuda":
+        raise ValueError("inputs must be GPU tensors")
     if (tk is None) != (tv is None):
         raise ValueError("tk and tv must both be None (frozen context) or both tensors")
     ins = [x for x in (q, k, v, tq, tk, tv) if x is not None]
@@ -204,6 +218,10 @@ def fwd_part(q, k, v, tq, tk, tv, k0, k1, scale=None, out=None, stream=None):
         tlse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
     else:
         o, to, lse, tlse = out
+        _check_out(o, q.shape, q.dtype, q.device, "o")
+        _check_out(to, q.shape, q.dtype, q.device, "to")
+        _check_out(lse, (B, H, Lq), torch.float32, q.device, "lse")
+        _check_out(tlse, (B, H, Lq), torch.float32, q.device, "tlse")
     off = k0 * d * k.element_size()
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     tk_p = None if tk is None else tk.data_ptr() + off
@@ -223,6 +241,10 @@ def merge(parts, out=None, stream=None):
     if not 1 <= len(parts) <= ATTN_JVP_MAX_MERGE_PARTS:
         raise ValueError(f"1 .. {ATTN_JVP_MAX_MERGE_PARTS} parts")
     o0 = parts[0][0]
+    if o0.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("o must be float32 or bfloat16")
+    if o0.device.type != "cuda":
+        raise ValueError("parts must be GPU tensors")
     dtype = ATTN_JVP_BF16 if o0.dtype == torch.bfloat16 else ATTN_JVP_FP32
     d = o0.shape[-1]
     rows = o0.numel() // d
@@ -233,11 +255,17 @@ def merge(parts, out=None, stream=None):
             raise ValueError("all parts: lse and tlse float32 with one value per row")
         if not all(x.is_contiguous() for x in (o, to, lse, tlse)):
             raise ValueError("all parts contiguous")
+        if any(x.device != o0.device for x in (o, to, lse, tlse)):
+            raise ValueError("all parts on one device")
     if out is None:
         o, to = torch.empty_like(o0), torch.empty_like(o0)
         lse, tlse = torch.empty_like(parts[0][2]), torch.empty_like(parts[0][3])
     else:
         o, to, lse, tlse = out
+        _check_out(o, o0.shape, o0.dtype, o0.device, "o")
+        _check_out(to, o0.shape, o0.dtype, o0.device, "to")
+        _check_out(lse, parts[0][2].shape, torch.float32, o0.device, "lse")
+        _check_out(tlse, parts[0][2].shape, torch.float32, o0.device, "tlse")
     s = stream if stream is not None else torch.cuda.current_stream(o0.device)
     status = attn_jvp_merge(len(parts), [p[0] for p in parts], [p[1] for p in parts], [p[2] for p in parts],
                             [p[3] for p in parts], o, to, lse, tlse, rows, d, dtype, s.cuda_stream)
@@ -279,6 +307,8 @@ def proj(x, tx, w, bias=None, n_out=3, heads=None, out=None, stream=None):
         raise ValueError("heads is required")
     if x.dtype != torch.bfloat16:
         raise TypeError("the projection takes bfloat16 tensors")
+    if x.device.type != "cuda":
+        raise ValueError("inputs must be GPU tensors")
     ins = [t for t in (x, tx, w, bias) if t is not None]
     if any(t.dtype != x.dtype or t.device != x.device or not t.is_contiguous() for t in ins):
         raise ValueError("all inputs: bfloat16, one device, contiguous")
@@ -297,6 +327,12 @@ def proj(x, tx, w, bias=None, n_out=3, heads=None, out=None, stream=None):
         ty = torch.empty(shape, dtype=x.dtype, device=x.device) if tx is not None else None
     else:
         y, ty = out
+        _check_out(y, shape, x.dtype, x.device, "y")
+        if tx is None:
+            if ty is not None:
+                raise ValueError("ty must be None without a tangent")
+        else:
+            _check_out(ty, shape, x.dtype, x.device, "ty")
     s = stream if stream is not None else torch.cuda.current_stream(x.device)
     status = attn_jvp_proj(x, tx, w, bias, y, ty, B, L, D, n_out, heads, d, ATTN_JVP_BF16, s.cuda_stream)
     if status != ATTN_JVP_OK:

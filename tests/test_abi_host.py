@@ -252,3 +252,22 @@ def test_absurd_sizes_are_rejected_without_overflow(lib):
     for kw in (dict(n_out=1 << 40, H=1 << 40), dict(L=big), dict(B=big), dict(D=big - 3),
                dict(n_out=(1 << 31) - 1, H=(1 << 31) - 1)):
         assert call_proj(**kw) == A.ATTN_JVP_EUNSUPPORTED, kw
+
+
+def test_binding_rejects_host_tensors():
+    """The torch wrappers refuse CPU tensors before any library call (their
+    addresses would be host memory)."""
+    import torch
+
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        A.fwd(q, q, q, q, q, q)
+    with pytest.raises(ValueError, match="GPU"):
+        A.fwd_part(q, q, q, q, q, q, 0, 4)
+    lse = torch.zeros(1, 1, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        A.merge([(q, q, lse, lse)])
+    x = torch.zeros(1, 8, 64, dtype=torch.bfloat16)
+    w = torch.zeros(3 * 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        A.proj(x, x, w, n_out=3, heads=1)

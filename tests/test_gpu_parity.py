@@ -140,6 +140,35 @@ def test_outputs_fully_written_and_guard_bands(A, dtype, d):
     check(w, compare(w, o, to, lse))
 
 
+def test_wrong_output_buffers_are_rejected(A):
+    """Caller-provided outputs must have exactly the extent the kernels write:
+    a wrong shape, dtype, device or layout raises before any launch."""
+    w = custom_workload(1, 2, 70, 90, 64, "bf16", seed_id=2600)
+    print("case wrong output buffers", flush=True)
+    x = device_inputs(w)
+    args = (x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"])
+    q = x["q"]
+    good = (torch.empty_like(q), torch.empty_like(q), torch.empty((1, 2, 70), dtype=torch.float32, device="cuda"))
+    bad = [
+        (torch.empty((1, 2, 69, 64), dtype=q.dtype, device="cuda"), good[1], good[2]),
+        (good[0], torch.empty_like(q, dtype=torch.float32), good[2]),
+        (good[0], good[1], torch.empty((1, 2, 70), dtype=torch.bfloat16, device="cuda")),
+        (good[0], torch.empty((1, 2, 64, 70), dtype=q.dtype, device="cuda").transpose(2, 3), good[2]),
+        (good[0], good[1], torch.empty((1, 2, 70))),
+    ]
+    for out in bad:
+        with pytest.raises(ValueError):
+            A.fwd(*args, out=out)
+    with pytest.raises(ValueError):
+        A.fwd_part(*args, 0, 64, out=good + (torch.empty((1, 2, 71), device="cuda"),))
+    parts = [A.fwd_part(*args, a, b) for a, b in ((0, 64), (64, 90))]
+    with pytest.raises(ValueError):
+        A.merge(parts, out=good + (torch.empty((1, 2, 7), device="cuda"),))
+    o, to, lse = A.fwd(*args, out=good)  # the right buffers still work
+    torch.cuda.synchronize()
+    check(w, compare(w, o, to, lse))
+
+
 def test_bitwise_deterministic_and_streams(A):
     w = custom_workload(1, 4, 333, 1000, 128, "bf16", seed_id=3002)
     print("case determinism", flush=True)

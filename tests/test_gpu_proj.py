@@ -95,6 +95,19 @@ def test_outputs_stay_inside_their_buffers(A):
         assert not bool((b[guard:guard + n] == sentinel).any())
 
 
+def test_wrong_output_buffers_are_rejected(A):
+    w = custom_proj(1, 40, 64, 3, 2, 64, seed_id=2202)
+    print("case proj wrong output buffers", flush=True)
+    x = device_proj_inputs(w)
+    y = torch.empty(w.out_shape, dtype=torch.bfloat16, device="cuda")
+    short = torch.empty((3, 1, 2, 39, 64), dtype=torch.bfloat16, device="cuda")
+    for out in ((short, y), (y, short), (y, y.float()), (y, None)):
+        with pytest.raises(ValueError):
+            A.proj(x["x"], x["tx"], x["w"], x["bias"], n_out=3, heads=2, out=out)
+    with pytest.raises(ValueError):
+        A.proj(x["x"], None, x["w"], x["bias"], n_out=3, heads=2, out=(y, y))
+
+
 def test_bitwise_deterministic(A):
     w = custom_proj(1, 260, 256, 3, 2, 128, seed_id=2202)
     print("case proj determinism", flush=True)
