@@ -78,6 +78,28 @@ def test_ragged_shapes(A, B, H, Lq, Lk, d, dtype):
     check(w, compare(w, o, to, lse))
 
 
+LONG_FP32 = [
+    # (B, H, Lq, Lk, d, logit std per operand, tangent std, rising-logit ramp, frozen)
+    (1, 1, 4064, 6082, 64, 2.0, 10.0, 0.0, False),
+    (2, 2, 339, 2219, 128, 2.0, 0.5, 0.0, False),
+    (2, 1, 349, 1500, 128, 2.0, 10.0, 0.0, True),
+]
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,d,sq,st,ramp,frozen", LONG_FP32)
+def test_fp32_long_sums_peaky_logits(A, B, H, Lq, Lk, d, sq, st, ramp, frozen):
+    """fp32 at its 1e-5 tolerance on long key ranges with peaky logits and large
+    tangents, where one fp32 chain over all keys had drifted to 2e-5."""
+    std = {"q": sq, "k": sq, "v": 1.0, "tq": st, "tk": 0.0 if frozen else st, "tv": 0.0 if frozen else st}
+    w = custom_workload(B, H, Lq, Lk, d, "fp32", seed_id=3300 + Lk, std=std, key_ramp=ramp)
+    print(f"case fp32 long sums B{B} H{H} Lq{Lq} Lk{Lk} d{d} sq{sq} st{st} ramp{ramp} frozen={frozen}", flush=True)
+    x = device_inputs(w)
+    tk, tv = (None, None) if frozen else (x["tk"], x["tv"])
+    o, to, lse = A.fwd(x["q"], x["k"], x["v"], x["tq"], tk, tv, scale=w.scale)
+    torch.cuda.synchronize()
+    check(w, compare(w, o, to, lse))
+
+
 def test_image_self_bf16(A):
     w = WORKLOADS["image_self_bf16"]
     print(f"case {w.name} (all rows)", flush=True)
