@@ -134,21 +134,28 @@ void attn_jvp_fp32_kernel(Params p) {
   auto accumulate = [&](const char* cur, const float (&pv)[16], const float (&ptv)[16]) {
     const char* vbase = cur + 2 * C::kTile;
     const char* tvbase = cur + 3 * C::kTile;
+    // Block b's partial sums are added to the totals under block b + 1's first
+    // MFMAs, not right behind their own last one.
+    f32x16 to_[2], tt_[2];
 #pragma unroll
     for (int b = 0; b < C::kBlocksD; ++b) {
-      f32x16 to_, tt_;
+      const int k = b & 1;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const uint32_t off = (acc_row(r, hh) * D + 32 * b + n) * 4;
         const float vv = *reinterpret_cast<const float*>(vbase + off);
         const float tvv = *reinterpret_cast<const float*>(tvbase + off);
-        to_ = mfma(vv, pv[r], r == 0 ? f32x16{} : to_);
-        tt_ = mfma(tvv, pv[r], r == 0 ? f32x16{} : tt_);
-        tt_ = mfma(vv, ptv[r], tt_);
+        to_[k] = mfma(vv, pv[r], r == 0 ? f32x16{} : to_[k]);
+        tt_[k] = mfma(tvv, pv[r], r == 0 ? f32x16{} : tt_[k]);
+        tt_[k] = mfma(vv, ptv[r], tt_[k]);
+        if (b > 0 && r == 1) {
+          acc_o[b - 1] += to_[k ^ 1];
+          acc_t[b - 1] += tt_[k ^ 1];
+        }
       }
-      acc_o[b] += to_;
-      acc_t[b] += tt_;
     }
+    acc_o[C::kBlocksD - 1] += to_[(C::kBlocksD - 1) & 1];
+    acc_t[C::kBlocksD - 1] += tt_[(C::kBlocksD - 1) & 1];
   };
 
   // Tile j lives in LDS stage j & 1; tile j + 1 is copied while tile j is used
