@@ -275,15 +275,21 @@ def bench_proj(args):
 
 
 def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="video_self_bf16")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=30.0)
-    ap.add_argument("--cpu-rows-per-head", type=int, default=1024)
-    ap.add_argument("--copy-calibration", action="store_true")
+    from workloads import WORKLOADS
+
+    ap = argparse.ArgumentParser(description="Attention forward + JVP (or projection) throughput on one MI355X; "
+                                             "prints one JSON line.")
+    ap.add_argument("--gpus", type=int, default=1, help="must be 1: the library runs on one GPU")
+    ap.add_argument("--steps", type=int, default=20, help="timed launches")
+    ap.add_argument("--warmup", type=int, default=3, help="untimed launches before them")
+    ap.add_argument("--workload", default="video_self_bf16", choices=sorted(WORKLOADS),
+                    help="attention workload (default: the 32760-token video self-attention layer)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the fp64 oracle on the host")
+    ap.add_argument("--cpu-budget", type=float, default=30.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--cpu-rows-per-head", type=int, default=1024,
+                    help="query rows per head that the CPU baseline times (then extrapolated)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy instead (HBM counter calibration)")
     ap.add_argument("--split", type=int, default=0,
                     help="time the key-sharded path: N attn_jvp_fwd_part passes plus attn_jvp_merge; "
                          "the roofline object then covers the merge launch (HBM bound)")
@@ -316,8 +322,6 @@ def main():
     import torch
 
     import attention_forward_mode_attn_amd as A
-    from workloads import WORKLOADS
-
     from workloads.device import device_inputs
 
     w = WORKLOADS[args.workload]
