@@ -84,3 +84,63 @@ def test_projection_random_shape(A, i, B, L, D, n_out, H, d, tangent, bias):
             continue
         err = np.abs(got.float().cpu().numpy() - ref)
         assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 2e-4 * np.abs(ref).max()), float(err.max())
+
+
+def distribution_cases(n=24, seed=20261205):
+    """Seeded shapes with varied value distributions: operand std (logit std is
+    its square at the default scale), tangent std, softmax scale, key shards up
+    to 16, and fp32 over long key ranges, inside the envelope fp32 can meet."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = str(rng.choice(["bf16", "fp32"]))
+        d = int(rng.choice([64, 128]))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        Lq = int(rng.integers(1, 600))
+        Lk = int(rng.integers(1, 9000 if dtype == "fp32" else 12000))
+        sq = float(rng.choice([0.3, 1.0, 2.0] if dtype == "fp32" else [0.3, 1.0, 2.0, 2.83]))
+        st = float(rng.choice([0.01, 0.5, 1.0, 10.0]))
+        scale = float(10 ** rng.uniform(-2.5, -0.5))
+        if dtype == "fp32":
+            # logit std sq^2 * scale * sqrt(d) at most 4: inside what fp32 logits can
+            # carry to the 1e-5 tolerance over these key ranges
+            scale = min(scale, 4.0 / (sq * sq * d ** 0.5))
+        n_split = int(rng.choice([1, 1, 2, 5, 16])) if Lk >= 16 else 1
+        frozen = bool(rng.random() < 0.25)
+        out.append((i, B, H, Lq, Lk, d, dtype, sq, st, scale, n_split, frozen))
+    return out
+
+
+@pytest.mark.parametrize("i,B,H,Lq,Lk,d,dtype,sq,st,scale,n_split,frozen", distribution_cases())
+def test_attention_random_distribution(A, i, B, H, Lq, Lk, d, dtype, sq, st, scale, n_split, frozen):
+    std = {"q": sq, "k": sq, "v": 1.0, "tq": st, "tk": 0.0 if frozen else st, "tv": 0.0 if frozen else st}
+    w = custom_workload(B, H, Lq, Lk, d, dtype, seed_id=9500 + i, std=std)
+    # the oracle reads the softmax scale from the workload: give this one its own
+    w = _with_scale(w, scale)
+    print(f"case random distribution {i}: B{B} H{H} Lq{Lq} Lk{Lk} d{d} {dtype} sq={sq} st={st} "
+          f"scale={scale:.4g} split={n_split} frozen={frozen}", flush=True)
+    x = device_inputs(w)
+    tk, tv = (None, None) if frozen else (x["tk"], x["tv"])
+    if n_split == 1:
+        o, to, lse = A.fwd(x["q"], x["k"], x["v"], x["tq"], tk, tv, scale=scale)
+    else:
+        o, to, lse, _ = A.fwd_split(x["q"], x["k"], x["v"], x["tq"], tk, tv, n_split, scale=scale)
+    torch.cuda.synchronize()
+    res = compare(w, o, to, lse)
+    print(f"  O {res['O']:.3e} tO {res['tO']:.3e} lse {res['lse']:.3e}", flush=True)
+    assert res["O"] <= TOL[dtype] and res["tO"] <= TOL[dtype] and res["lse"] <= LSE_TOL[dtype]
+
+
+def _with_scale(w, scale):
+    """A copy of workload ``w`` whose softmax scale is ``scale``."""
+    import copy
+
+    class Scaled(type(w)):
+        @property
+        def scale(self):
+            return self._scale
+
+    w2 = copy.copy(w)
+    object.__setattr__(w2, "__class__", Scaled)
+    object.__setattr__(w2, "_scale", scale)
+    return w2
