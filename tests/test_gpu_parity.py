@@ -128,6 +128,13 @@ def test_video_self_bf16_sampled(A):
     check(w, compare(w, o, to, lse, rows_fn=lambda b, h: sample_rows(w, b, h)), per_head_gate=True)
 
 
+def test_video_self_d64_bf16_sampled(A):
+    w = WORKLOADS["video_self_d64_bf16"]
+    print(f"case {w.name} (256 sampled rows per head)", flush=True)
+    _, o, to, lse = run(A, w)
+    check(w, compare(w, o, to, lse, rows_fn=lambda b, h: sample_rows(w, b, h)), per_head_gate=True)
+
+
 def test_video_cross_stress_bf16_sampled(A):
     w = WORKLOADS["video_cross_stress_bf16"]
     print(f"case {w.name} (256 sampled rows per head)", flush=True)

@@ -95,6 +95,10 @@ WORKLOADS = {
             description="video-token self-attention JVP (21x30x52 latent tokens), one GPU's layer",
         ),
         Workload(
+            "video_self_d64_bf16", 7, B=1, H=80, Lq=32760, Lk=32760, d=64, dtype="bf16", std=_std(),
+            description="the video self-attention layer's width split into 80 heads of 64",
+        ),
+        Workload(
             "video_cross_stress_bf16", 5, B=1, H=40, Lq=32760, Lk=512, d=128, dtype="bf16",
             std=_std(q=_SQRT8, k=_SQRT8), per_head_tq_scale=True,
             description="video cross-attention with peaky softmax (logit std ~ 8) and "
