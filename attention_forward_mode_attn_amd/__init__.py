@@ -163,7 +163,8 @@ def fwd(q, k, v, tq, tk, tv, scale=None, out=None, stream=None):
         _check_out(to, q.shape, q.dtype, q.device, "to")
         _check_out(lse, (B, H, Lq), torch.float32, q.device, "lse")
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
-    status = attn_jvp_fwd(q, k, v, tq, tk, tv, o, to, lse, B, H, Lq, Lk, d, scale, dtype, s.cuda_stream)
+    with torch.cuda.device(q.device):  # launch on the inputs' device
+        status = attn_jvp_fwd(q, k, v, tq, tk, tv, o, to, lse, B, H, Lq, Lk, d, scale, dtype, s.cuda_stream)
     if status != ATTN_JVP_OK:
         raise AttnJvpError(status, attn_jvp_last_error())
     return o, to, lse
@@ -226,8 +227,9 @@ def fwd_part(q, k, v, tq, tk, tv, k0, k1, scale=None, out=None, stream=None):
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     tk_p = None if tk is None else tk.data_ptr() + off
     tv_p = None if tv is None else tv.data_ptr() + off
-    status = attn_jvp_fwd_part(q, k.data_ptr() + off, v.data_ptr() + off, tq, tk_p, tv_p, o, to, lse, tlse,
-                               B, H, Lq, k1 - k0, Lk, d, scale, dtype, s.cuda_stream)
+    with torch.cuda.device(q.device):
+        status = attn_jvp_fwd_part(q, k.data_ptr() + off, v.data_ptr() + off, tq, tk_p, tv_p, o, to, lse, tlse,
+                                   B, H, Lq, k1 - k0, Lk, d, scale, dtype, s.cuda_stream)
     if status != ATTN_JVP_OK:
         raise AttnJvpError(status, attn_jvp_last_error())
     return o, to, lse, tlse
@@ -267,8 +269,9 @@ def merge(parts, out=None, stream=None):
         _check_out(lse, parts[0][2].shape, torch.float32, o0.device, "lse")
         _check_out(tlse, parts[0][2].shape, torch.float32, o0.device, "tlse")
     s = stream if stream is not None else torch.cuda.current_stream(o0.device)
-    status = attn_jvp_merge(len(parts), [p[0] for p in parts], [p[1] for p in parts], [p[2] for p in parts],
-                            [p[3] for p in parts], o, to, lse, tlse, rows, d, dtype, s.cuda_stream)
+    with torch.cuda.device(o0.device):
+        status = attn_jvp_merge(len(parts), [p[0] for p in parts], [p[1] for p in parts], [p[2] for p in parts],
+                                [p[3] for p in parts], o, to, lse, tlse, rows, d, dtype, s.cuda_stream)
     if status != ATTN_JVP_OK:
         raise AttnJvpError(status, attn_jvp_last_error())
     return o, to, lse, tlse
@@ -334,7 +337,8 @@ def proj(x, tx, w, bias=None, n_out=3, heads=None, out=None, stream=None):
         else:
             _check_out(ty, shape, x.dtype, x.device, "ty")
     s = stream if stream is not None else torch.cuda.current_stream(x.device)
-    status = attn_jvp_proj(x, tx, w, bias, y, ty, B, L, D, n_out, heads, d, ATTN_JVP_BF16, s.cuda_stream)
+    with torch.cuda.device(x.device):
+        status = attn_jvp_proj(x, tx, w, bias, y, ty, B, L, D, n_out, heads, d, ATTN_JVP_BF16, s.cuda_stream)
     if status != ATTN_JVP_OK:
         raise AttnJvpError(status, attn_jvp_last_error())
     return y, ty
