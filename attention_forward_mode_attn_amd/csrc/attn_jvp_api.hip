@@ -22,6 +22,10 @@ int fail(int status, const char* what) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Every kernel runs a 1-D grid of 256-thread workgroups, and a launch must
+// keep gridDim.x * blockDim.x below 2^32: at most 2^24 - 1 workgroups.
+constexpr int64_t kMaxWorkgroups = (int64_t(1) << 24) - 1;
+
 }  // namespace
 
 extern "C" {
@@ -66,8 +70,8 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* tq, const 
   if (Lq >= lim / d || Lk >= lim / d) return fail(ATTN_JVP_EUNSUPPORTED, "sequence too long for one head");
   if (kv_rows > INT32_MAX) return fail(ATTN_JVP_EUNSUPPORTED, "kv_rows too large");
   const int64_t qtiles = (Lq + 127) / 128;
-  if (B > INT32_MAX || H > INT32_MAX || B * H > INT32_MAX || B * H * qtiles >= (int64_t(1) << 31))
-    return fail(ATTN_JVP_EUNSUPPORTED, "too many workgroups");
+  if (B > kMaxWorkgroups || H > kMaxWorkgroups || B * H > kMaxWorkgroups || B * H * qtiles > kMaxWorkgroups)
+    return fail(ATTN_JVP_EUNSUPPORTED, "too many workgroups: B*H*ceil(Lq/128) must stay below 2^24");
 
   attnjvp::Problem p;
   p.q = q; p.k = k; p.v = v; p.tq = tq; p.tk = tk; p.tv = tv;
@@ -110,7 +114,9 @@ int attn_jvp_merge(int n, const void* const* o_parts, const void* const* to_part
   if (rows < 0 || d < 0) return fail(ATTN_JVP_EINVAL, "negative size");
   if (d != 64 && d != 128) return fail(ATTN_JVP_EUNSUPPORTED, "head dimension must be 64 or 128");
   if (rows == 0) return ATTN_JVP_OK;
-  if (rows / (256 / (d / 8)) >= INT32_MAX) return fail(ATTN_JVP_EUNSUPPORTED, "too many rows");
+  const int64_t rows_per_block = 256 / (d / 8);
+  if ((rows + rows_per_block - 1) / rows_per_block > kMaxWorkgroups)
+    return fail(ATTN_JVP_EUNSUPPORTED, "too many rows: ceil(rows*d/2048) must stay below 2^24");
   if (!o_parts || !to_parts || !lse_parts || !tlse_parts || !o || !to || !lse)
     return fail(ATTN_JVP_EINVAL, "NULL pointer");
   attnjvp::MergeProblem p{};
@@ -166,7 +172,8 @@ int attn_jvp_proj(const void* x, const void* tx, const void* w, const void* bias
   if (F >= lim || L * D >= lim || F * D >= lim || L * d >= lim)
     return fail(ATTN_JVP_EUNSUPPORTED, "size beyond the projection's limits");
   const int64_t blocks = ((F + 255) / 256) * ((L + 127) / 128) * B;
-  if (blocks >= lim) return fail(ATTN_JVP_EUNSUPPORTED, "too many workgroups");
+  if (blocks > kMaxWorkgroups)
+    return fail(ATTN_JVP_EUNSUPPORTED, "too many workgroups: B*ceil(L/128)*ceil(n_out*H*d/256) must stay below 2^24");
   attnjvp::ProjProblem p;
   p.x = x; p.tx = tx; p.w = w; p.bias = bias; p.y = y; p.ty = ty;
   p.B = (int)B; p.L = (int)L; p.D = (int)D; p.n_out = (int)n_out; p.H = (int)H; p.d = (int)d;

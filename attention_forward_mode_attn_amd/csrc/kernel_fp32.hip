@@ -285,8 +285,7 @@ hipError_t launch(const Problem& pr, hipStream_t stream) {
   p.Lq = pr.Lq; p.Lk = pr.Lk; p.kv_rows = pr.kv_rows; p.scale = pr.scale;
   p.n_qtiles = (pr.Lq + kBlockRows - 1) / kBlockRows;
   p.n_blocks = pr.B * pr.H * p.n_qtiles;
-  hipLaunchKernelGGL(attn_jvp_fp32_kernel<D>, dim3(p.n_blocks), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  return launch_1d(reinterpret_cast<const void*>(&attn_jvp_fp32_kernel<D>), p.n_blocks, kThreads, p, stream);
 }
 
 }  // namespace

@@ -4,6 +4,17 @@
 
 namespace attnjvp {
 
+// Enqueue `kernel`, whose one parameter is the by-value struct `a`, on a 1-D
+// grid, and return the status of this launch itself.  (Reading
+// hipGetLastError() after a launch would also return, and clear, an error
+// that an unrelated earlier call left pending on the calling thread.)
+template <typename Args>
+inline hipError_t launch_1d(const void* kernel, unsigned blocks, unsigned threads, const Args& a,
+                            hipStream_t stream) {
+  void* args[] = {const_cast<Args*>(&a)};
+  return hipLaunchKernel(kernel, dim3(blocks), dim3(threads), args, 0, stream);
+}
+
 struct Problem {
   const void* q;
   const void* k;

@@ -115,8 +115,7 @@ hipError_t launch(const MergeProblem& p, hipStream_t stream) {
   constexpr int kRowsPerBlock = 256 / (D / 8);
   const int64_t blocks = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
   MergeArgs a{p};
-  hipLaunchKernelGGL((merge_kernel<BF16, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_1d(reinterpret_cast<const void*>(&merge_kernel<BF16, D>), (unsigned)blocks, 256, a, stream);
 }
 
 }  // namespace

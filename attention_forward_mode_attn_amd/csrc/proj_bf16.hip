@@ -326,8 +326,7 @@ hipError_t launch(const ProjProblem& pr, hipStream_t stream) {
   p.n_tt = (p.L + kTT - 1) / kTT;
   p.n_blocks = p.n_ft * p.n_tt * p.B;
   p.group_f = p.n_blocks < kSmallGrid ? kGroupFSmall : kGroupFLarge;
-  hipLaunchKernelGGL((proj_bf16_kernel<kT>), dim3(p.n_blocks), dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
+  return launch_1d(reinterpret_cast<const void*>(&proj_bf16_kernel<kT>), p.n_blocks, kThreads, p, stream);
 }
 
 }  // namespace

@@ -16,6 +16,13 @@ Other modes:
                        tangent).  Same JSON contract.
   --copy-calibration   time/profile a plain device copy of known size (HBM
                        counter calibration) instead of the kernel.
+  --trace-summary DIR  summarise a rocprofv3 kernel-trace (or counter) CSV
+                       under DIR: per-kernel dispatch statistics, skipping the
+                       first --skip dispatches of each kernel (the warm-ups).
+
+The default run also times the other attention workloads (tiny fp32, image
+self-attention, text cross-attention with and without the frozen-context path,
+the video cross-attention stress case) and reports them under "per_workload".
 """
 from __future__ import annotations
 
@@ -194,6 +201,130 @@ def cpu_baseline_proj(w, h, budget_s: float = 30.0):
     }
 
 
+def time_launches(step, stream, warmup: int, n: int):
+    """Run ``step`` warmup + n times on ``stream``; per-launch HIP-event times
+    (ms) of the last n, sorted."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)
+
+
+# The workloads timed beside the headline one in the default run: name, whether
+# the frozen-context path (tk = tv = NULL) is used, timed launches.
+PER_WORKLOAD = (
+    ("tiny_self_fp32", False, 50),
+    ("image_self_bf16", False, 20),
+    ("text_cross_bf16", False, 50),
+    ("text_cross_bf16", True, 50),
+    ("video_cross_stress_bf16", False, 20),
+)
+
+
+def per_workload(warmup: int = 3):
+    """Timed figures of the other attention workloads: average, median
+    and minimum launch time over the timed launches (HIP events on the launch
+    stream, after ``warmup`` untimed launches), TFLOP/s of the nominal
+    12*B*H*Lq*Lk*d flops (of the executed 8*B*H*Lq*Lk*d on the frozen-context
+    path) and the fraction of the dtype's peak."""
+    import torch
+
+    import attention_forward_mode_attn_amd as A
+    from workloads import WORKLOADS
+    from workloads.device import device_inputs
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    cache = {}
+    for name, frozen, n in PER_WORKLOAD:
+        w = WORKLOADS[name]
+        print(f"bench: per-workload {name}{' (frozen context)' if frozen else ''}", file=sys.stderr, flush=True)
+        if name not in cache:
+            cache.clear()
+            cache[name] = device_inputs(w)
+        x = cache[name]
+        o, to = torch.empty_like(x["q"]), torch.empty_like(x["q"])
+        lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device=dev)
+        tk, tv = (None, None) if frozen else (x["tk"], x["tv"])
+
+        def step():
+            A.fwd(x["q"], x["k"], x["v"], x["tq"], tk, tv, scale=w.scale, out=(o, to, lse), stream=stream)
+
+        ms = time_launches(step, stream, warmup, n)
+        avg = sum(ms) / len(ms)
+        flops = w.flops * (8.0 / 12.0 if frozen else 1.0)
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        tf = flops / (avg * 1e-3) / 1e12
+        out[name + ("_frozen" if frozen else "")] = {
+            "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "d": w.d, "dtype": w.dtype,
+            "path": "frozen context (tk = tv = NULL), executed 8 flops per logit and head dim" if frozen
+                    else "full JVP, 12 flops per logit and head dim",
+            "launches": n, "warmup": warmup,
+            "avg_launch_ms": round(avg, 5), "median_launch_ms": round(ms[len(ms) // 2], 5),
+            "min_launch_ms": round(ms[0], 5),
+            "flops_per_launch": flops, "tflops": round(tf, 2), "peak": peak, "frac": round(tf / peak, 4),
+        }
+    return out
+
+
+def trace_summary(directory: str, skip: int, kernel_filter: str = ""):
+    """Per-kernel dispatch statistics of a rocprofv3 CSV run under
+    ``directory``: the kernel trace (``*kernel_trace.csv``) gives durations from
+    the dispatch timestamps; a counter run (``*counter_collection.csv``) gives
+    each dispatch's counters.  The first ``skip`` dispatches of every kernel are
+    left out (the untimed warm-up launches of the run)."""
+    import csv
+    import glob
+
+    out = {}
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)):
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+        per = {}
+        for r in rows:
+            name = r.get("Kernel_Name", "")
+            if kernel_filter and kernel_filter not in name:
+                continue
+            per.setdefault(name, []).append((int(r["Dispatch_Id"]),
+                                             int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        for name, ds in per.items():
+            ds.sort()
+            dur = [t for _, t in ds[skip:]]
+            if not dur:
+                continue
+            s = sorted(dur)
+            out.setdefault("kernel_trace", {})[name] = {
+                "dispatches": len(ds), "skipped": min(skip, len(ds)), "counted": len(dur),
+                "avg_ns": sum(dur) / len(dur), "median_ns": s[len(s) // 2], "min_ns": s[0], "max_ns": s[-1],
+                "durations_ns": dur,
+            }
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)):
+        with open(path) as f:
+            rows = list(csv.DictReader(f))
+        per = {}
+        for r in rows:
+            name = r.get("Kernel_Name", "")
+            if kernel_filter and kernel_filter not in name:
+                continue
+            d = per.setdefault(name, {}).setdefault(int(r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if "Start_Timestamp" in r and "End_Timestamp" in r:
+                d["_duration_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        for name, ds in per.items():
+            keys = sorted(ds)[skip:]
+            out.setdefault("counters", {})[name] = [dict(dispatch=k, **ds[k]) for k in keys]
+    return out
+
+
 def bench_proj(args):
     import torch
 
@@ -298,7 +429,18 @@ def main():
                          "value is then executed TFLOP/s at 8 flops per logit and head dim")
     ap.add_argument("--proj", default=None,
                     help="time the projection into attention heads (attn_jvp_proj) on this projection workload")
+    ap.add_argument("--no-per-workload", action="store_true",
+                    help="skip timing the other attention workloads (the per_workload object)")
+    ap.add_argument("--trace-summary", default=None, metavar="DIR",
+                    help="print per-kernel statistics of the rocprofv3 CSV output under DIR as JSON and exit")
+    ap.add_argument("--skip", type=int, default=0,
+                    help="with --trace-summary: dispatches of each kernel left out at the start (warm-ups)")
+    ap.add_argument("--kernel", default="", help="with --trace-summary: only kernels whose name contains this")
     args = ap.parse_args()
+
+    if args.trace_summary is not None:
+        print(json.dumps(trace_summary(args.trace_summary, args.skip, args.kernel)))
+        return
 
     if args.split and not 1 <= args.split <= 16:
         print("bench.py: --split must be in 1 .. 16 (ATTN_JVP_MAX_MERGE_PARTS)", file=sys.stderr)
@@ -461,6 +603,9 @@ def main():
         "sclk_mhz": sclk,
         "roofline": roofline,
     }
+    if args.workload == "video_self_bf16" and not (args.split or args.frozen_context or args.no_per_workload):
+        del x, o, to, lse
+        out["per_workload"] = per_workload()
     if not args.no_cpu_baseline:
         print("bench: timing the fp64 oracle on sampled rows (cpu_baseline)", file=sys.stderr, flush=True)
         cb = cpu_baseline(w, args.cpu_budget, args.cpu_rows_per_head)

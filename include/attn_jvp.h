@@ -92,7 +92,10 @@ typedef enum {
  * failed check launches nothing.  Exactly one of tk, tv NULL is
  * ATTN_JVP_EINVAL.  B*H*Lq == 0 is a no-op returning ATTN_JVP_OK
  * (pointers are then not inspected).  Limits: Lq*d and Lk*d below 2^29
- * elements per head, B*H*ceil(Lq/128) below 2^31.  The library never aborts.
+ * elements per head; B*H*ceil(Lq/128), the number of 256-thread workgroups,
+ * below 2^24 (a launch keeps its thread count below 2^32); beyond them the
+ * call returns ATTN_JVP_EUNSUPPORTED and launches nothing.  The library never
+ * aborts.
  * Non-finite input values propagate into the outputs; they are not detected.
  */
 int attn_jvp_fwd(const void* q, const void* k, const void* v,
@@ -154,6 +157,8 @@ int attn_jvp_fwd_part(const void* q, const void* k, const void* v,
  * Ownership, alignment (16 bytes for [rows, d] tensors, 4 for [rows]),
  * execution and errors follow attn_jvp_fwd; rows == 0 is a no-op; outputs must
  * not overlap any input.  The host arrays are read during the call only.
+ * Limit: ceil(rows*d/2048) (the workgroup count) below 2^24, else
+ * ATTN_JVP_EUNSUPPORTED.
  */
 int attn_jvp_merge(int n, const void* const* o_parts, const void* const* to_parts,
                    const float* const* lse_parts, const float* const* tlse_parts,
@@ -197,7 +202,9 @@ int attn_jvp_merge(int n, const void* const* o_parts, const void* const* to_part
  * Layout, ownership, alignment (16 bytes for every pointer), execution and
  * errors follow attn_jvp_fwd.  Exactly one of tx, ty NULL is ATTN_JVP_EINVAL;
  * B*L == 0 or n_out*H == 0 is a no-op.  Limits: L*D, n_out*H*d*D and L*d below
- * 2^31 elements, D below 2^22.  Outputs must not overlap any input.
+ * 2^31 elements, D below 2^22, and B*ceil(L/128)*ceil(n_out*H*d/256) (the
+ * workgroup count) below 2^24; beyond them ATTN_JVP_EUNSUPPORTED.  Outputs must
+ * not overlap any input.
  */
 int attn_jvp_proj(const void* x, const void* tx, const void* w, const void* bias,
                   void* y, void* ty,

@@ -271,3 +271,32 @@ def test_binding_rejects_host_tensors():
     w = torch.zeros(3 * 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         A.proj(x, x, w, n_out=3, heads=1)
+
+
+def test_grids_of_2_24_workgroups_are_rejected_on_host(lib):
+    """Every kernel launches a 1-D grid of 256-thread workgroups, and a launch
+    keeps gridDim.x * 256 below 2^32: exactly 2^24 workgroups must fail the host
+    check (EUNSUPPORTED, nothing launched), not the launch."""
+    # attention: B*H*ceil(Lq/128) = 2^24
+    assert call(B=1, H=1 << 24, Lq=1, Lk=1, d=64) == A.ATTN_JVP_EUNSUPPORTED
+    assert "2^24" in A.attn_jvp_last_error()
+    assert call(B=1 << 12, H=1 << 5, Lq=128 * (1 << 7), Lk=8, d=64) == A.ATTN_JVP_EUNSUPPORTED
+    assert call_part(B=1 << 24) == A.ATTN_JVP_EUNSUPPORTED
+    # merge: ceil(rows / (256 / (d / 8))) = 2^24 (16 rows per workgroup at d = 128)
+    assert call_merge(rows=(1 << 24) * 16, d=128) == A.ATTN_JVP_EUNSUPPORTED
+    assert call_merge(rows=(1 << 24) * 32, d=64) == A.ATTN_JVP_EUNSUPPORTED
+    # projection: B*ceil(L/128)*ceil(n_out*H*d/256) = 2^24
+    assert call_proj(B=1 << 24, L=1, n_out=1, H=2, d=128) == A.ATTN_JVP_EUNSUPPORTED
+    assert call_proj(B=1 << 14, L=128 * 1024, D=64, n_out=1, H=2, d=128) == A.ATTN_JVP_EUNSUPPORTED
+
+
+def test_grids_just_below_2_24_workgroups_pass_host_checks(lib):
+    """2^24 - 1 workgroups is the largest grid: the call passes every host
+    check and, with no GPU present, reaches the launch (ELAUNCH)."""
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this checks the no-device path only")
+    assert call(B=1, H=(1 << 24) - 1, Lq=1, Lk=1, d=64) == A.ATTN_JVP_ELAUNCH
+    assert call_merge(rows=((1 << 24) - 1) * 16, d=128) == A.ATTN_JVP_ELAUNCH
+    assert call_proj(B=(1 << 24) - 1, L=1, n_out=1, H=2, d=128) == A.ATTN_JVP_ELAUNCH

@@ -68,3 +68,29 @@ def test_sclk_parsing_and_sampling(tmp_path):
     assert bench.wait_sampling_sclk(str(f), Pending(2), period_s=0.0, min_samples=3) is None  # too short a run
     assert bench.wait_sampling_sclk(None, Pending(3), period_s=0.0) is None
     assert bench.wait_sampling_sclk(str(f), Pending(0), period_s=0.0) is None
+
+
+def test_trace_summary_skips_warmups(tmp_path):
+    """--trace-summary reads rocprofv3's kernel-trace and counter CSVs and
+    leaves out the first --skip dispatches of each kernel."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    d = tmp_path / "host" / "run"
+    d.mkdir(parents=True)
+    hdr = "Kind,Agent_Id,Queue_Id,Dispatch_Id,Kernel_Id,Kernel_Name,Start_Timestamp,End_Timestamp\n"
+    rows = [(1, "k<a>", 0, 900), (2, "other", 0, 5), (3, "k<a>", 1000, 1100), (4, "k<a>", 2000, 2120),
+            (5, "k<a>", 3000, 3110)]
+    (d / "run_kernel_trace.csv").write_text(
+        hdr + "".join(f"KERNEL_DISPATCH,1,1,{i},7,\"{n}\",{s},{e}\n" for i, n, s, e in rows))
+    chdr = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n"
+    crow = [(1, "k<a>", "X", 3.0, 0, 50), (1, "k<a>", "X", 4.0, 0, 50), (3, "k<a>", "X", 5.0, 60, 80)]
+    (d / "run_counter_collection.csv").write_text(
+        chdr + "".join(f"{i},\"{n}\",{c},{v},{s},{e}\n" for i, n, c, v, s, e in crow))
+    out = bench.trace_summary(str(tmp_path), skip=1, kernel_filter="k<")
+    k = out["kernel_trace"]["k<a>"]
+    assert k["dispatches"] == 4 and k["counted"] == 3 and k["durations_ns"] == [100, 120, 110]
+    assert k["avg_ns"] == 110 and k["min_ns"] == 100 and k["max_ns"] == 120
+    assert "other" not in out["kernel_trace"]
+    c = out["counters"]["k<a>"]
+    assert c == [{"dispatch": 3, "X": 5.0, "_duration_ns": 20}]

@@ -64,3 +64,19 @@ def test_split_bench_line_reports_the_merge():
     check_common(d, 3, 1, "text_cross_bf16", "bf16")
     assert d["roofline"]["bound"] == "hbm" and d["roofline"]["unit"] == "GB/s"
     assert "cpu_baseline" not in d
+
+
+def test_default_bench_line_carries_every_workload():
+    """The default run (the video self-attention headline) also times the other
+    attention workloads and reports each under per_workload."""
+    d = bench("--steps", "2", "--warmup", "1", "--no-cpu-baseline")
+    check_common(d, 2, 1, "video_self_bf16", "bf16")
+    pw = d["per_workload"]
+    assert sorted(pw) == ["image_self_bf16", "text_cross_bf16", "text_cross_bf16_frozen", "tiny_self_fp32",
+                          "video_cross_stress_bf16"]
+    for name, e in pw.items():
+        assert e["launches"] >= 10 and e["avg_launch_ms"] > 0 and e["tflops"] > 0, name
+        assert abs(e["frac"] - e["tflops"] / e["peak"]) < 1e-3, name
+        assert abs(e["tflops"] - e["flops_per_launch"] / (e["avg_launch_ms"] * 1e-3) / 1e12) < 1e-2 * e["tflops"]
+    assert pw["tiny_self_fp32"]["peak"] == 157.3 and pw["image_self_bf16"]["peak"] == 2500.0
+    assert pw["text_cross_bf16_frozen"]["flops_per_launch"] * 1.5 == pw["text_cross_bf16"]["flops_per_launch"]
