@@ -301,9 +301,9 @@ void attn_jvp_bf16_kernel(Params p) {
   // Softmax element e: p = 2^y, q = p * ts.  P and P*tS become bf16 B
   // operands, packed in pairs: chunk cc (keys 16cc..16cc+15) is elements
   // 8cc .. 8cc + 7.  l += p is summed in fp32 (it sets O's normaliser and the
-  // log-sum-exp); a += q is taken over the packed bf16 pairs (one dot2 with
-  // (1, 1) per pair), the same rounded values that the tO products consume.
-  // Four steps per element: exp; q and l; pack (odd e); a and the operands.
+  // log-sum-exp); a += q is taken over the packed bf16 pairs (sum_a), the same
+  // rounded values that the tO products consume.
+  // Four steps per element: exp; q and l; pack (odd e); the operands.
   struct Probs {
     bf16x8 pf[4], ptf[4];
     float p[32], q[32];
@@ -328,13 +328,25 @@ void attn_jvp_bf16_kernel(Params p) {
       }
     } else if constexpr (e & 1) {
       constexpr int cc = e >> 3, i = (e & 7) - 1;
-      st.a = sum_bf16x2(pr.qq[e >> 1], st.a);
-      pin(st.a);
       pr.pf[cc][i] = __builtin_bit_cast(bf16x2, pr.pp[e >> 1])[0];
       pr.pf[cc][i + 1] = __builtin_bit_cast(bf16x2, pr.pp[e >> 1])[1];
       pr.ptf[cc][i] = __builtin_bit_cast(bf16x2, pr.qq[e >> 1])[0];
       pr.ptf[cc][i + 1] = __builtin_bit_cast(bf16x2, pr.qq[e >> 1])[1];
     }
+  };
+  // a += the 32 rounded products of the tile: one v_dot2 with (1, 1) per
+  // packed pair, all 16 in one unit as four independent chains.  On gfx950 the
+  // first v_dot2 after an MFMA waits ~17 cycles and each further one issues in
+  // 4, so one batch per tile costs ~80 cycles where a v_dot2 in every other
+  // unit cost ~270.
+  auto sum_a = [&](const Probs& pr) {
+    float s4[4];
+    static_for<0, 16>([&](auto ix) {
+      constexpr int x = decltype(ix)::value;
+      s4[x & 3] = sum_bf16x2(pr.qq[x], x == 0 ? st.a : (x < 4 ? 0.0f : s4[x & 3]));
+    });
+    st.a = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    pin(st.a);
   };
   // Software pipeline over a sequence of N units that handle n items (N
   // units, items [g n / N, (g + 1) n / N) start in unit g): unit g runs step s
@@ -412,6 +424,7 @@ void attn_jvp_bf16_kernel(Params p) {
   constexpr int kUnitsA = kUPC * C::kChunksD;  // logit MFMAs of one tile
   constexpr int kPreSlots = 2;               // softmax slots run before the first logit MFMA
   constexpr int kUnitsB = (kFrozen ? 8 : 12) * C::kBlocksD;  // MFMAs of products(), 0 .. kUnitsB - 1
+  constexpr int kSumAUnit = 3 - kPreSlots;  // first phase-B unit after the tile's last softmax step
 
   const int nt = (Lk + kBc - 1) / kBc;
   const bool ragged = (Lk % kBc) != 0;
@@ -498,6 +511,7 @@ void attn_jvp_bf16_kernel(Params p) {
       // (they complete chunk 3, which the products reach last)
       if constexpr (unit + kPreSlots < 3)
         pipeline_slot(IC<kUnitsA + kPreSlots + unit>{}, IC<kUnitsA>{}, IC<32>{}, IC<4>{}, elem);
+      if constexpr (unit == kSumAUnit) sum_a(pr);  // every pair of the tile is packed by now
       pipeline_slot(iunit, IC<kUnitsB>{}, IC<64>{}, IC<3>{}, take);
     });
     pipeline_slot(IC<kUnitsB>{}, IC<kUnitsB>{}, IC<64>{}, IC<3>{}, take);
@@ -553,6 +567,7 @@ void attn_jvp_bf16_kernel(Params p) {
   {  // drain: the last tile's probabilities and products
     Probs pr;
     all_steps(IC<0>{}, IC<32>{}, IC<4>{}, [&](auto is, auto ie) { elem_step(is, ie, pr); });
+    sum_a(pr);
     bf16x8 vf[C::kBlocksD], tvf[C::kBlocksD];
     load_v0(smem + (j & 1) * C::kStage, vf, tvf);
     products(smem + (j & 1) * C::kStage, pr, vf, tvf, [](auto) {});

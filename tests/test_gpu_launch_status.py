@@ -2,7 +2,9 @@
 
 An error that an unrelated earlier HIP call left pending on the calling thread
 (here an invalid hipSetDevice) must neither fail a correct launch nor be
-consumed by it: the call returns ATTN_JVP_OK and the outputs match the oracle.
+consumed by it: the call returns ATTN_JVP_OK, the caller still finds its own
+error pending afterwards (read here with hipGetLastError, which also clears it
+before torch's next call would report it), and the outputs match the oracle.
 """
 import ctypes
 
@@ -28,15 +30,30 @@ def A():
     return A
 
 
-def leave_pending_error():
-    """A failed HIP call on this thread: hipSetDevice with an ordinal far past
-    the device count returns hipErrorInvalidDevice and changes nothing else."""
+HIP_ERROR_INVALID_DEVICE = 101
+
+
+def _hip():
     hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch and the library share
     hip.hipSetDevice.argtypes = [ctypes.c_int]
     hip.hipSetDevice.restype = ctypes.c_int
-    rc = hip.hipSetDevice(9999)
-    assert rc != 0, "hipSetDevice(9999) unexpectedly succeeded"
+    hip.hipGetLastError.argtypes = []
+    hip.hipGetLastError.restype = ctypes.c_int
     return hip
+
+
+def leave_pending_error():
+    """A failed HIP call on this thread: hipSetDevice with an ordinal far past
+    the device count returns hipErrorInvalidDevice and changes nothing else."""
+    hip = _hip()
+    hip.hipGetLastError()  # start from a clean state
+    rc = hip.hipSetDevice(9999)
+    assert rc == HIP_ERROR_INVALID_DEVICE, rc
+
+
+def pending_error_survived():
+    """The planted error is still the thread's last error (and is cleared now)."""
+    return _hip().hipGetLastError() == HIP_ERROR_INVALID_DEVICE
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -44,9 +61,12 @@ def test_pending_error_does_not_fail_attention(A, dtype):
     w = custom_workload(1, 2, 150, 90, 64, dtype, seed_id=5151)
     print(f"case pending-error fwd {w.name} {dtype}", flush=True)
     x = device_inputs(w)
+    o, to = torch.empty_like(x["q"]), torch.empty_like(x["q"])
+    lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device=x["q"].device)
     torch.cuda.synchronize()
     leave_pending_error()
-    o, to, lse = A.fwd(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], scale=w.scale)
+    A.fwd(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], scale=w.scale, out=(o, to, lse))  # raises if not OK
+    assert pending_error_survived()
     torch.cuda.synchronize()
     res = compare(w, o, to, lse)
     assert res["O"] <= TOL[dtype] and res["tO"] <= TOL[dtype] and res["lse"] <= LSE_TOL[dtype], res
@@ -56,10 +76,26 @@ def test_pending_error_does_not_fail_merge_or_projection(A):
     w = custom_workload(1, 2, 130, 200, 128, "bf16", seed_id=5152)
     print(f"case pending-error split+merge {w.name}", flush=True)
     x = device_inputs(w)
+    bounds = A.shard_bounds(w.Lk, 3)
+    lse_shape = (w.B, w.H, w.Lq)
+
+    def four():
+        return (torch.empty_like(x["q"]), torch.empty_like(x["q"]),
+                torch.empty(lse_shape, dtype=torch.float32, device=x["q"].device),
+                torch.empty(lse_shape, dtype=torch.float32, device=x["q"].device))
+
+    parts = [four() for _ in bounds]
+    merged = four()
     torch.cuda.synchronize()
+    for (k0, k1), part in zip(bounds, parts):
+        leave_pending_error()
+        A.fwd_part(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], k0, k1, scale=w.scale, out=part)
+        assert pending_error_survived()
     leave_pending_error()
-    o, to, lse, _ = A.fwd_split(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], 3, scale=w.scale)
+    A.merge(parts, out=merged)
+    assert pending_error_survived()
     torch.cuda.synchronize()
+    o, to, lse, _ = merged
     res = compare(w, o, to, lse)
     assert res["O"] <= TOL["bf16"] and res["tO"] <= TOL["bf16"], res
 
@@ -69,9 +105,12 @@ def test_pending_error_does_not_fail_merge_or_projection(A):
     print(f"case pending-error projection {pw.name}", flush=True)
     h = proj_host_inputs(pw)
     xp = device_proj_inputs(pw, device="cuda:0")
+    y = torch.empty((3, 1, 2, 70, 64), dtype=torch.bfloat16, device="cuda:0")
+    ty = torch.empty_like(y)
     torch.cuda.synchronize()
     leave_pending_error()
-    y, ty = A.proj(xp["x"], xp["tx"], xp["w"], xp["bias"], n_out=3, heads=2)
+    A.proj(xp["x"], xp["tx"], xp["w"], xp["bias"], n_out=3, heads=2, out=(y, ty))
+    assert pending_error_survived()
     torch.cuda.synchronize()
     Y, TY = projection_jvp(h["x"], h["tx"], h["w"], h["bias"], 3, 2, 64)
     for got, ref in ((y, Y), (ty, TY)):
