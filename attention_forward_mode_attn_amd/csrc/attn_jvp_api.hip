@@ -115,7 +115,7 @@ int attn_jvp_merge(int n, const void* const* o_parts, const void* const* to_part
   if (d != 64 && d != 128) return fail(ATTN_JVP_EUNSUPPORTED, "head dimension must be 64 or 128");
   if (rows == 0) return ATTN_JVP_OK;
   const int64_t rows_per_block = 256 / (d / 8);
-  if ((rows + rows_per_block - 1) / rows_per_block > kMaxWorkgroups)
+  if (rows > kMaxWorkgroups * rows_per_block)  // more than kMaxWorkgroups workgroups
     return fail(ATTN_JVP_EUNSUPPORTED, "too many rows: ceil(rows*d/2048) must stay below 2^24");
   if (!o_parts || !to_parts || !lse_parts || !tlse_parts || !o || !to || !lse)
     return fail(ATTN_JVP_EINVAL, "NULL pointer");
@@ -171,8 +171,8 @@ int attn_jvp_proj(const void* x, const void* tx, const void* w, const void* bias
   const int64_t F = n_out * H * d;
   if (F >= lim || L * D >= lim || F * D >= lim || L * d >= lim)
     return fail(ATTN_JVP_EUNSUPPORTED, "size beyond the projection's limits");
-  const int64_t blocks = ((F + 255) / 256) * ((L + 127) / 128) * B;
-  if (blocks > kMaxWorkgroups)
+  const int64_t tiles = ((F + 255) / 256) * ((L + 127) / 128);  // < 2^23 * 2^24: no overflow
+  if (B > kMaxWorkgroups || tiles > kMaxWorkgroups || tiles * B > kMaxWorkgroups)
     return fail(ATTN_JVP_EUNSUPPORTED, "too many workgroups: B*ceil(L/128)*ceil(n_out*H*d/256) must stay below 2^24");
   attnjvp::ProjProblem p;
   p.x = x; p.tx = tx; p.w = w; p.bias = bias; p.y = y; p.ty = ty;
