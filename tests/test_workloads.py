@@ -110,3 +110,24 @@ def test_projection_inputs_are_seeded_bf16_values():
     video = PROJ_WORKLOADS["qkv_video_bf16"]
     assert video.F == 15360 and video.D == video.H * video.d
     assert video.flops == 4.0 * 32760 * 5120 * 15360
+
+
+def test_norm_rope_inputs_are_seeded_and_rounded():
+    import numpy as np
+
+    from workloads import NORM_ROPE_WORKLOADS, custom_norm_rope, norm_rope_array, norm_rope_upload, rope_tables
+    from workloads.inputs import bf16_bits_to_f32
+
+    w = NORM_ROPE_WORKLOADS["q_image_bf16"]
+    a = norm_rope_array(w, "x", 1, 3)
+    assert a.shape == (w.L, w.d) and np.array_equal(a, norm_rope_array(w, "x", 1, 3))
+    assert not np.array_equal(a, norm_rope_array(w, "x", 1, 2))
+    assert np.array_equal(bf16_bits_to_f32(norm_rope_upload(w, "x", 1, 3)), a)
+    g = norm_rope_array(w, "gamma")
+    assert g.shape == (w.d,) and abs(float(g.mean()) - 1.0) < 0.05
+    c, s = rope_tables(w)
+    assert c.shape == (w.L, w.d // 2) and c.dtype == np.float32
+    assert np.allclose(c[0], 1.0) and np.allclose(s[0], 0.0)       # position 0: no rotation
+    assert np.allclose(c * c + s * s, 1.0, atol=1e-6)
+    f = custom_norm_rope(1, 1, 3, 64, dtype="fp32", rope=False)
+    assert rope_tables(f) == (None, None) and norm_rope_array(f, "x").dtype == np.float32

@@ -14,6 +14,15 @@ from .inputs import (  # noqa: F401
     sample_rows,
     tq_head_scale,
 )
+from .norm_rope import (  # noqa: F401
+    NORM_ROPE_TENSORS,
+    NORM_ROPE_WORKLOADS,
+    NormRopeWorkload,
+    custom_norm_rope,
+    norm_rope_array,
+    norm_rope_upload,
+    rope_tables,
+)
 from .proj import (  # noqa: F401
     PROJ_TENSORS,
     PROJ_WORKLOADS,

@@ -50,3 +50,31 @@ def device_proj_inputs(w, device="cuda"):
     out["w"] = up(proj_upload(w, "w"))
     out["bias"] = up(proj_upload(w, "bias")) if w.bias else None
     return out
+
+
+def device_norm_rope_inputs(w, device="cuda", threads=8):
+    """The inputs of norm/rope workload ``w`` on ``device``: x, tx [B, H, L, d]
+    (tx None without tangent), gamma [d] (None without gain), cos, sin [L, d/2]
+    float32 (None without rotation)."""
+    import torch
+
+    from .norm_rope import norm_rope_upload, rope_tables
+
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def up(arr):
+        return (torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16) if w.dtype == "bf16"
+                else torch.from_numpy(arr))
+
+    names = ("x", "tx") if w.tangent else ("x",)
+    out = {t: torch.empty(w.shape(), dtype=tdt, device=device) for t in names}
+    jobs = [(t, b, h) for t in names for b in range(w.B) for h in range(w.H)]
+    with ThreadPoolExecutor(threads) as ex:
+        for (t, b, h), arr in ex.map(lambda j: (j, norm_rope_upload(w, *j)), jobs):
+            out[t][b, h].copy_(up(arr))
+    out.setdefault("tx", None)
+    out["gamma"] = up(norm_rope_upload(w, "gamma")).to(device) if w.gain else None
+    c, s = rope_tables(w)
+    out["cos"] = torch.from_numpy(c).to(device) if c is not None else None
+    out["sin"] = torch.from_numpy(s).to(device) if s is not None else None
+    return out
