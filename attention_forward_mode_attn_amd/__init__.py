@@ -4,8 +4,9 @@ The functions below carry the C ABI's names and only marshal arguments; every
 step of the computation runs in the HIP kernels of the library.  ``fwd`` is a
 convenience wrapper that allocates the outputs with torch and raises on error;
 ``fwd_part``, ``merge`` and ``fwd_split`` do the same for the key-sharded
-partial passes and their exact merge, and ``proj`` for the projection of
-hidden states into attention heads with its tangent.
+partial passes and their exact merge, ``proj`` for the projection of
+hidden states into attention heads with its tangent, and ``rmsnorm_rope`` for
+the RMS normalisation and rotary embedding of queries or keys with theirs.
 There is no fallback: if the library is missing, every call raises.
 """
 from __future__ import annotations
@@ -17,8 +18,8 @@ __all__ = [
     "ATTN_JVP_FP32", "ATTN_JVP_BF16", "ATTN_JVP_OK", "ATTN_JVP_EINVAL", "ATTN_JVP_EUNSUPPORTED",
     "ATTN_JVP_EALIGN", "ATTN_JVP_ELAUNCH", "ATTN_JVP_MAX_MERGE_PARTS", "AttnJvpError", "attn_jvp_fwd",
     "attn_jvp_fwd_part", "attn_jvp_merge", "attn_jvp_status_string", "attn_jvp_last_error",
-    "attn_jvp_version", "attn_jvp_proj", "fwd", "fwd_part", "merge", "fwd_split", "shard_bounds", "proj",
-    "library_path", "load_library",
+    "attn_jvp_version", "attn_jvp_proj", "attn_jvp_rmsnorm_rope", "fwd", "fwd_part", "merge", "fwd_split",
+    "shard_bounds", "proj", "rmsnorm_rope", "library_path", "load_library",
 ]
 
 ATTN_JVP_FP32, ATTN_JVP_BF16 = 0, 1
@@ -61,6 +62,8 @@ def load_library() -> ctypes.CDLL:
     lib.attn_jvp_merge.restype = ctypes.c_int
     lib.attn_jvp_proj.argtypes = [vp] * 6 + [i64] * 6 + [ctypes.c_int, vp]
     lib.attn_jvp_proj.restype = ctypes.c_int
+    lib.attn_jvp_rmsnorm_rope.argtypes = [vp] * 7 + [i64] * 4 + [ctypes.c_float, ctypes.c_int, vp]
+    lib.attn_jvp_rmsnorm_rope.restype = ctypes.c_int
     lib.attn_jvp_status_string.argtypes = [ctypes.c_int]
     lib.attn_jvp_status_string.restype = ctypes.c_char_p
     lib.attn_jvp_last_error.argtypes = []
@@ -125,6 +128,16 @@ def attn_jvp_proj(x, tx, w, bias, y, ty, B, L, D, n_out, H, d, dtype, stream=Non
     return int(lib.attn_jvp_proj(
         _ptr(x), _ptr(tx), _ptr(w), _ptr(bias), _ptr(y), _ptr(ty),
         int(B), int(L), int(D), int(n_out), int(H), int(d), int(dtype), stream,
+    ))
+
+
+def attn_jvp_rmsnorm_rope(x, tx, y, ty, gamma, rope_cos, rope_sin, B, H, L, d, eps, dtype, stream=None) -> int:
+    """Marshal to the C entry point (tx, ty, gamma, rope_cos, rope_sin may be
+    None).  Returns the status code."""
+    lib = load_library()
+    return int(lib.attn_jvp_rmsnorm_rope(
+        _ptr(x), _ptr(tx), _ptr(y), _ptr(ty), _ptr(gamma), _ptr(rope_cos), _ptr(rope_sin),
+        int(B), int(H), int(L), int(d), float(eps), int(dtype), stream,
     ))
 
 
@@ -339,6 +352,59 @@ def proj(x, tx, w, bias=None, n_out=3, heads=None, out=None, stream=None):
     s = stream if stream is not None else torch.cuda.current_stream(x.device)
     with torch.cuda.device(x.device):
         status = attn_jvp_proj(x, tx, w, bias, y, ty, B, L, D, n_out, heads, d, ATTN_JVP_BF16, s.cuda_stream)
+    if status != ATTN_JVP_OK:
+        raise AttnJvpError(status, attn_jvp_last_error())
+    return y, ty
+
+
+def rmsnorm_rope(x, tx=None, gamma=None, rope_cos=None, rope_sin=None, eps=1e-6, out=None, inplace=False,
+                 stream=None):
+    """RMS normalisation over the head dim with gain ``gamma`` [d] (None: 1),
+    then rotation of adjacent pairs by the angles of each row's position
+    (``rope_cos``, ``rope_sin`` float32 [L, d/2], both None: no rotation), for
+    torch tensors x [B, H, L, d] (float32 or bfloat16) and its tangent tx (or
+    None).  Returns (y, ty); ``inplace=True`` writes into x and tx,
+    ``out=(y, ty)`` into given buffers."""
+    import torch
+
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    if x.device.type != "cuda":
+        raise ValueError("inputs must be GPU tensors")
+    if x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, H, L, d] tensor")
+    B, H, L, d = x.shape
+    if tx is not None and (tx.shape != x.shape or tx.dtype != x.dtype or tx.device != x.device
+                           or not tx.is_contiguous()):
+        raise ValueError("tx must match x")
+    if gamma is not None and (gamma.shape != (d,) or gamma.dtype != x.dtype or gamma.device != x.device):
+        raise ValueError("gamma must be [d] in x's dtype on x's device")
+    if (rope_cos is None) != (rope_sin is None):
+        raise ValueError("rope_cos and rope_sin must both be given or both be None")
+    for tab in (rope_cos, rope_sin):
+        if tab is not None and (tab.shape != (L, d // 2) or tab.dtype != torch.float32 or tab.device != x.device
+                                or not tab.is_contiguous()):
+            raise ValueError("rope tables must be contiguous float32 [L, d/2] on x's device")
+    if inplace:
+        if out is not None:
+            raise ValueError("out and inplace are exclusive")
+        y, ty = x, tx
+    elif out is None:
+        y = torch.empty_like(x)
+        ty = torch.empty_like(x) if tx is not None else None
+    else:
+        y, ty = out
+        _check_out(y, x.shape, x.dtype, x.device, "y")
+        if tx is None:
+            if ty is not None:
+                raise ValueError("ty must be None without a tangent")
+        else:
+            _check_out(ty, x.shape, x.dtype, x.device, "ty")
+    dtype = ATTN_JVP_BF16 if x.dtype == torch.bfloat16 else ATTN_JVP_FP32
+    s = stream if stream is not None else torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        status = attn_jvp_rmsnorm_rope(x, tx, y, ty, gamma, rope_cos, rope_sin, B, H, L, d, eps, dtype,
+                                       s.cuda_stream)
     if status != ATTN_JVP_OK:
         raise AttnJvpError(status, attn_jvp_last_error())
     return y, ty

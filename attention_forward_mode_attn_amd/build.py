@@ -31,7 +31,7 @@ CFLAGS = [
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]
-SOURCES = ["kernel_bf16.hip", "kernel_fp32.hip", "merge.hip", "proj_bf16.hip", "attn_jvp_api.hip"]
+SOURCES = ["kernel_bf16.hip", "kernel_fp32.hip", "merge.hip", "proj_bf16.hip", "norm_rope.hip", "attn_jvp_api.hip"]
 
 
 def _run(cmd, verbose):

@@ -185,4 +185,38 @@ int attn_jvp_proj(const void* x, const void* tx, const void* w, const void* bias
   return ATTN_JVP_OK;
 }
 
+int attn_jvp_rmsnorm_rope(const void* x, const void* tx, void* y, void* ty, const void* gamma, const float* rope_cos,
+                          const float* rope_sin, int64_t B, int64_t H, int64_t L, int64_t d, float eps, int dtype,
+                          void* stream) {
+  g_last_error[0] = '\0';
+  if (dtype != ATTN_JVP_FP32 && dtype != ATTN_JVP_BF16) return fail(ATTN_JVP_EINVAL, "dtype must be 0 (fp32) or 1 (bf16)");
+  if (B < 0 || H < 0 || L < 0 || d < 0) return fail(ATTN_JVP_EINVAL, "negative size");
+  if (d != 64 && d != 128) return fail(ATTN_JVP_EUNSUPPORTED, "head dimension must be 64 or 128");
+  if (B == 0 || H == 0 || L == 0) return ATTN_JVP_OK;  // nothing to compute
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(ATTN_JVP_EINVAL, "eps must be finite and >= 0");
+  if (!x || !y) return fail(ATTN_JVP_EINVAL, "NULL pointer");
+  if ((tx == nullptr) != (ty == nullptr)) return fail(ATTN_JVP_EINVAL, "tx and ty must both be NULL or both non-NULL");
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(ATTN_JVP_EINVAL, "rope_cos and rope_sin must both be NULL or both non-NULL");
+  const void* p16[] = {x, tx, y, ty, gamma, rope_cos, rope_sin};
+  for (const void* q : p16)
+    if (!aligned(q, 16)) return fail(ATTN_JVP_EALIGN, "pointers must be 16-byte aligned");
+  // Every factor is bounded before it is multiplied.
+  if (B > kMaxWorkgroups || H > kMaxWorkgroups || B * H > kMaxWorkgroups || L > INT32_MAX)
+    return fail(ATTN_JVP_EUNSUPPORTED, "size beyond the limits");
+  const int64_t rows_per_block = 256 / (d * (dtype == ATTN_JVP_BF16 ? 2 : 4) / 16);
+  if (((L + rows_per_block - 1) / rows_per_block) * (B * H) > kMaxWorkgroups)
+    return fail(ATTN_JVP_EUNSUPPORTED, "too many workgroups: B*H*ceil(L/rows per workgroup) must stay below 2^24");
+  attnjvp::NormRopeProblem p{};
+  p.x = x; p.tx = tx; p.y = y; p.ty = ty; p.gamma = gamma; p.cos = rope_cos; p.sin = rope_sin;
+  p.BH = (int)(B * H); p.L = (int)L; p.d = (int)d; p.eps = eps; p.bf16 = dtype == ATTN_JVP_BF16;
+  const hipError_t e = attnjvp::launch_norm_rope(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    std::snprintf(g_last_error, sizeof g_last_error, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+    return ATTN_JVP_ELAUNCH;
+  }
+  return ATTN_JVP_OK;
+}
+
 }  // extern "C"
+

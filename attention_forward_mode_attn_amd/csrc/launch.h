@@ -66,4 +66,20 @@ struct ProjProblem {
 
 hipError_t launch_proj(const ProjProblem& p, hipStream_t stream);
 
+struct NormRopeProblem {
+  const void* x;
+  const void* tx;     // null: no tangent (ty null too)
+  void* y;            // may equal x
+  void* ty;           // may equal tx
+  const void* gamma;  // [d] in the element type, or null (gain 1)
+  const float* cos;   // [L, d/2], or null together with sin (no rotation)
+  const float* sin;
+  int BH, L, d;       // validated: d in {64, 128}, BH * L > 0
+  int n_blocks;       // set by the launcher
+  float eps;
+  bool bf16;
+};
+
+hipError_t launch_norm_rope(const NormRopeProblem& p, hipStream_t stream);
+
 }  // namespace attnjvp

@@ -14,6 +14,10 @@ Other modes:
                        (qkv_video_bf16: 32760 tokens, D = 5120 -> 3 x 40 x 128);
                        throughput counts 2*B*L*D*F flops per product (two with a
                        tangent).  Same JSON contract.
+  --norm-rope NAME     time attn_jvp_rmsnorm_rope, the RMS normalisation and rotary
+                       embedding of queries or keys with the tangent (q_video_bf16:
+                       40 heads x 32760 rows of 128); bound by HBM traffic, so the
+                       roofline is in GB/s of its algorithmic bytes.
   --copy-calibration   time/profile a plain device copy of known size (HBM
                        counter calibration) instead of the kernel.
   --trace-summary DIR  summarise a rocprofv3 kernel-trace (or counter) CSV
@@ -42,6 +46,7 @@ PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix/vector, vendor figure
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, vendor figure
 METRIC = "attention-JVP TFLOP/s (12*B*H*Lq*Lk*d) + % bf16 MFMA peak, 1 MI355X"
 METRIC_FROZEN = "attention-JVP executed TFLOP/s, frozen context (8*B*H*Lq*Lk*d) + % bf16 MFMA peak, 1 MI355X"
+METRIC_NORM_ROPE = "RMS-norm + rotary embedding JVP, HBM GB/s of algorithmic bytes (% of 8 TB/s), 1 MI355X"
 METRIC_PROJ = "projection-JVP TFLOP/s (2*B*L*D*F per product, X and TX) + % bf16 MFMA peak, 1 MI355X"
 # The sources of each kernel whose HBM traffic profiles/ records: a change to
 # any of them makes the recorded traffic stale (reported as null).
@@ -325,6 +330,116 @@ def trace_summary(directory: str, skip: int, kernel_filter: str = ""):
     return out
 
 
+def bench_norm_rope(args):
+    import torch
+
+    import attention_forward_mode_attn_amd as A
+    from workloads import NORM_ROPE_WORKLOADS
+    from workloads.device import device_norm_rope_inputs
+
+    w = NORM_ROPE_WORKLOADS[args.norm_rope]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"bench: {w.name} B{w.B} H{w.H} L{w.L} d{w.d} {w.dtype} tangent={w.tangent} rope={w.rope}: "
+          "generating inputs", file=sys.stderr, flush=True)
+    x = device_norm_rope_inputs(w)
+    y = torch.empty_like(x["x"])
+    ty = torch.empty_like(x["x"]) if w.tangent else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        A.rmsnorm_rope(x["x"], x["tx"], x["gamma"], x["cos"], x["sin"], eps=w.eps, out=(y, ty), stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for a, b in per:
+        a.record(stream)
+        step()
+        b.record(stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    launch_ms = sorted(a.elapsed_time(b) for a, b in per)
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    value = w.algorithmic_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = w.algorithmic_bytes / (avg_launch_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC_NORM_ROPE,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) rows and tangents, gain 1 + N(0, 0.1^2), rotary tables of positions 0..L-1)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "tangent": w.tangent,
+                   "rope": w.rope, "gain": w.gain, "eps": w.eps, "parallelism": "single GPU"},
+        "wall_s_timed_region": round(wall, 3),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "kernel": f"norm_rope_kernel<{str(w.dtype == 'bf16').lower()}, {w.d}>",
+            "avg_launch_ms": round(avg_launch_ms, 5),
+            "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 5),
+            "min_launch_ms": round(launch_ms[0], 5),
+            "algorithmic_bytes_per_launch": w.algorithmic_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the fp64 oracle on whole heads (cpu_baseline)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_norm_rope(w, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_norm_rope(w, budget_s: float = 30.0):
+    """Time the fp64 oracle over whole heads until the budget is spent, in GB/s
+    of the same algorithmic bytes per row."""
+    from oracle import norm_rope_jvp
+    from workloads import norm_rope_array, rope_tables
+
+    c, s = rope_tables(w)
+    g = norm_rope_array(w, "gamma") if w.gain else None
+    rows, t_total, heads = 0, 0.0, 0
+    for b in range(w.B):
+        for h in range(w.H):
+            x = norm_rope_array(w, "x", b, h)
+            tx = norm_rope_array(w, "tx", b, h) if w.tangent else None
+            t0 = time.perf_counter()
+            norm_rope_jvp(x, tx, g, c, s, w.eps)
+            t_total += time.perf_counter() - t0
+            rows += w.L
+            heads += 1
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    per_row = w.algorithmic_bytes / w.rows
+    return {
+        "value": rows * per_row / t_total / 1e9,
+        "unit": "GB/s",
+        "cores": _blas_cores(),
+        "kind": "oracle",
+        "sample": f"{heads} heads x {w.L} rows of {w.name}; {t_total:.2f} s; full workload extrapolates to "
+                  f"{t_total / rows * w.rows:.1f} s",
+        "float": "f64",
+    }
+
+
 def bench_proj(args):
     import torch
 
@@ -429,6 +544,9 @@ def main():
                          "value is then executed TFLOP/s at 8 flops per logit and head dim")
     ap.add_argument("--proj", default=None,
                     help="time the projection into attention heads (attn_jvp_proj) on this projection workload")
+    ap.add_argument("--norm-rope", default=None,
+                    help="time the RMS normalisation + rotary embedding of queries/keys (attn_jvp_rmsnorm_rope) "
+                         "on this workload")
     ap.add_argument("--no-per-workload", action="store_true",
                     help="skip timing the other attention workloads (the per_workload object)")
     ap.add_argument("--trace-summary", default=None, metavar="DIR",
@@ -450,6 +568,15 @@ def main():
               "(the attention JVP shards by (batch, head) with no exchange: run one process per GPU)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.norm_rope is not None:
+        from workloads import NORM_ROPE_WORKLOADS
+
+        if args.norm_rope not in NORM_ROPE_WORKLOADS or args.split or args.frozen_context or args.proj:
+            print(f"bench.py: --norm-rope takes one of {sorted(NORM_ROPE_WORKLOADS)} (alone)", file=sys.stderr)
+            sys.exit(2)
+        bench_norm_rope(args)
+        return
 
     if args.proj is not None:
         from workloads import PROJ_WORKLOADS

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define ATTN_JVP_VERSION 10200 /* 1.2.0 */
+#define ATTN_JVP_VERSION 10300 /* 1.3.0 */
 
 /* Largest number of partial results one attn_jvp_merge call combines. */
 #define ATTN_JVP_MAX_MERGE_PARTS 16
@@ -210,6 +210,51 @@ int attn_jvp_proj(const void* x, const void* tx, const void* w, const void* bias
                   void* y, void* ty,
                   int64_t B, int64_t L, int64_t D, int64_t n_out, int64_t H, int64_t d,
                   int dtype, void* stream);
+
+/*
+ * attn_jvp_rmsnorm_rope — RMS normalisation and rotary position embedding of
+ * the queries (or keys) of an attention layer, with the tangent: the layer
+ * between attn_jvp_proj and attn_jvp_fwd.
+ *
+ * The rCM pages make every layer take and return tangents and hand the
+ * tangents of Q and K to the attention kernel laid out like Q and K (ai.info
+ * summary of "Large Scale Diffusion Distillation via Score-Regularized
+ * Continuous-Time Consistency", "Methodology in Plain English" and "Key
+ * Contributions" item 1); they do not describe the layer itself.  This is the
+ * reading taken: each row x of d elements (token t of one head) is
+ * normalised by its root mean square with a gain g, then adjacent pairs
+ * (2i, 2i+1) are rotated by the angle of position t, given as tables; gain,
+ * eps and angles are constants (no tangent):
+ *
+ *   r  = (mean_j x_j^2 + eps)^(-1/2)        n  = g * x * r
+ *   tn = g * (tx * r - x * r^3 * mean_j x_j tx_j)
+ *   y_2i = c n_2i - s n_2i+1,  y_2i+1 = s n_2i + c n_2i+1   (c = cos[t,i], s = sin[t,i])
+ *   ty   = the same rotation of tn
+ *
+ * Arguments
+ *   x, tx      [B, H, L, d]  rows and their tangent (device, read only); tx and ty may
+ *                            both be NULL (no tangent)
+ *   y, ty      [B, H, L, d]  outputs (device, written); y may be x and ty may be tx
+ *                            (in place); any other overlap is undefined
+ *   gamma      [d] gain in the element type, or NULL (gain 1)     (device, read only)
+ *   rope_cos,  [L, d/2] float32 cos and sin of the angle of pair i at position t,
+ *   rope_sin   or both NULL (no rotation: normalisation only)     (device, read only)
+ *   B, H, L, d sizes; d in {64, 128}
+ *   eps        finite, >= 0
+ *   dtype      ATTN_JVP_BF16 (bf16 in and out, float32 arithmetic, outputs rounded to
+ *              nearest even) or ATTN_JVP_FP32
+ *   stream     as attn_jvp_fwd
+ *
+ * Alignment: every pointer 16 bytes.  Ownership, execution and errors follow
+ * attn_jvp_fwd; exactly one of tx, ty NULL, or one of rope_cos, rope_sin, or a
+ * negative or non-finite eps is ATTN_JVP_EINVAL; B*H*L == 0 is a no-op.
+ * Limits: B*H and the workgroup count B*H*ceil(L/R) below 2^24, where R =
+ * 2048/d rows per workgroup for bf16 and 1024/d for fp32; L below 2^31.
+ */
+int attn_jvp_rmsnorm_rope(const void* x, const void* tx, void* y, void* ty,
+                          const void* gamma, const float* rope_cos, const float* rope_sin,
+                          int64_t B, int64_t H, int64_t L, int64_t d, float eps,
+                          int dtype, void* stream);
 
 /* Static description of a status code ("unknown status" for others). */
 const char* attn_jvp_status_string(int status);

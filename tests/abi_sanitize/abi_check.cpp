@@ -74,6 +74,13 @@ static int proj(int64_t B, int64_t L, int64_t D, int64_t n_out, int64_t H, int64
                        tangent ? P(A0 + 80) : nullptr, B, L, D, n_out, H, d, 1, nullptr);
 }
 
+static int norm_rope(int64_t B, int64_t H, int64_t L, int64_t d, float eps = 1e-6f, int dtype = 1,
+                     bool tangent = true, bool tables = true) {
+  return attn_jvp_rmsnorm_rope(P(A0), tangent ? P(A0 + 16) : nullptr, P(A0 + 32), tangent ? P(A0 + 48) : nullptr,
+                               P(A0 + 64), tables ? F(A0 + 80) : nullptr, tables ? F(A0 + 96) : nullptr, B, H, L, d,
+                               eps, dtype, nullptr);
+}
+
 // The workgroup count each launcher derives from an accepted problem.
 static int64_t attn_blocks(const attnjvp::Problem& p) { return int64_t(p.B) * p.H * ((int64_t(p.Lq) + 127) / 128); }
 
@@ -96,6 +103,12 @@ int main() {
         stub::last_proj.L == 100 && stub::last_proj.D == 256 && stub::last_proj.n_out == 3);
   CHECK(proj(2, 100, 256, 2, 4, 128, false) == ATTN_JVP_OK && stub::last_proj.tx == nullptr);
 
+  CHECK(norm_rope(2, 3, 100, 128) == ATTN_JVP_OK && stub::last_kind == stub::Kind::norm_rope &&
+        stub::last_norm_rope.BH == 6 && stub::last_norm_rope.L == 100 && stub::last_norm_rope.d == 128 &&
+        stub::last_norm_rope.bf16 && stub::last_norm_rope.eps == 1e-6f);
+  CHECK(norm_rope(1, 1, 7, 64, 0.0f, 0, false, false) == ATTN_JVP_OK && stub::last_norm_rope.tx == nullptr &&
+        stub::last_norm_rope.cos == nullptr && !stub::last_norm_rope.bf16);
+
   // --- the largest accepted grids, and one workgroup more -----------------------
   const int64_t wg = (int64_t(1) << 24) - 1;
   CHECK(fwd(1, wg, 1, 1, 64) == ATTN_JVP_OK && attn_blocks(stub::last_problem) == wg);
@@ -108,6 +121,11 @@ int main() {
   CHECK(merge(2, wg * 32 + 1, 64) == ATTN_JVP_EUNSUPPORTED);
   CHECK(proj(wg, 1, 64, 1, 2, 128) == ATTN_JVP_OK);
   CHECK(proj(wg + 1, 1, 64, 1, 2, 128) == ATTN_JVP_EUNSUPPORTED);
+
+  CHECK(norm_rope(1, wg, 16, 128) == ATTN_JVP_OK);            // 16 rows per workgroup (bf16, d = 128)
+  CHECK(norm_rope(1, wg, 17, 128) == ATTN_JVP_EUNSUPPORTED);
+  CHECK(norm_rope(1, wg, 8, 128, 0.0f, 0) == ATTN_JVP_OK);     // 8 rows per workgroup (fp32, d = 128)
+  CHECK(norm_rope(1, wg, 9, 128, 0.0f, 0) == ATTN_JVP_EUNSUPPORTED);
 
   // --- stated size limits ---------------------------------------------------------
   CHECK(fwd(1, 1, (int64_t(1) << 22) - 1, 8, 128) == ATTN_JVP_OK);  // Lq*d just below 2^29
@@ -135,6 +153,11 @@ int main() {
   CHECK(merge(0, 8, 64) == ATTN_JVP_EINVAL && merge(17, 8, 64) == ATTN_JVP_EINVAL);
   CHECK(merge(2, 8, 100) == ATTN_JVP_EUNSUPPORTED && merge(2, -1, 64) == ATTN_JVP_EINVAL);
   CHECK(proj(1, 8, 96, 3, 2, 64) == ATTN_JVP_EUNSUPPORTED);
+  CHECK(norm_rope(1, 1, 8, 64, -1.0f) == ATTN_JVP_EINVAL && norm_rope(1, 1, 8, 64, INFINITY) == ATTN_JVP_EINVAL);
+  CHECK(attn_jvp_rmsnorm_rope(P(A0), P(A0), P(A0), nullptr, nullptr, nullptr, nullptr, 1, 1, 8, 64, 0.0f, 1,
+                              nullptr) == ATTN_JVP_EINVAL);
+  CHECK(attn_jvp_rmsnorm_rope(P(A0), nullptr, P(A0), nullptr, nullptr, F(A0), nullptr, 1, 1, 8, 64, 0.0f, 1,
+                              nullptr) == ATTN_JVP_EINVAL);
   CHECK(stub::calls == c0);
   CHECK(std::strlen(attn_jvp_last_error()) > 0);
 
@@ -173,12 +196,22 @@ int main() {
       const int s = proj(v[0], v[1], v[2], v[3], v[4], v[5]);
       CHECK(s == ATTN_JVP_OK || s == ATTN_JVP_EINVAL || s == ATTN_JVP_EUNSUPPORTED);
     }
+    for (int arg = 0; arg < 4; ++arg) {
+      int64_t v[4] = {2, 3, 100, 128};
+      v[arg] = x;
+      const int s = norm_rope(v[0], v[1], v[2], v[3]);
+      CHECK(s == ATTN_JVP_OK || s == ATTN_JVP_EINVAL || s == ATTN_JVP_EUNSUPPORTED);
+    }
     for (int64_t y : EXTREMES) {  // pairs of large factors
       int s = fwd(x, y, 1 << 20, 8, 64);
       CHECK(s != ATTN_JVP_OK || attn_blocks(stub::last_problem) <= wg);
       s = proj(x, y, 64, 1, 2, 128);
       CHECK(s == ATTN_JVP_OK || s == ATTN_JVP_EINVAL || s == ATTN_JVP_EUNSUPPORTED);
       s = proj(1, 1 << 20, 64, x, y, 128);
+      CHECK(s == ATTN_JVP_OK || s == ATTN_JVP_EINVAL || s == ATTN_JVP_EUNSUPPORTED);
+      s = norm_rope(x, y, 1 << 20, 64);
+      CHECK(s == ATTN_JVP_OK || s == ATTN_JVP_EINVAL || s == ATTN_JVP_EUNSUPPORTED);
+      s = norm_rope(1, x, y, 128, 0.0f, 0);
       CHECK(s == ATTN_JVP_OK || s == ATTN_JVP_EINVAL || s == ATTN_JVP_EUNSUPPORTED);
       s = proj(x, 1 << 24, 64, 1, y, 128);
       CHECK(s == ATTN_JVP_OK || s == ATTN_JVP_EINVAL || s == ATTN_JVP_EUNSUPPORTED);

@@ -13,6 +13,7 @@ Kind last_kind = Kind::none;
 attnjvp::Problem last_problem{};
 attnjvp::MergeProblem last_merge{};
 attnjvp::ProjProblem last_proj{};
+attnjvp::NormRopeProblem last_norm_rope{};
 hipError_t next_status = hipSuccess;
 }  // namespace stub
 
@@ -42,6 +43,11 @@ hipError_t launch_merge(const MergeProblem& p, hipStream_t) {
 hipError_t launch_proj(const ProjProblem& p, hipStream_t) {
   stub::last_proj = p;
   return record(stub::Kind::proj);
+}
+
+hipError_t launch_norm_rope(const NormRopeProblem& p, hipStream_t) {
+  stub::last_norm_rope = p;
+  return record(stub::Kind::norm_rope);
 }
 
 }  // namespace attnjvp

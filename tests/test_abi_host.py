@@ -31,13 +31,13 @@ def declared_functions():
 def test_library_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert names == ["attn_jvp_fwd", "attn_jvp_fwd_part", "attn_jvp_last_error", "attn_jvp_merge",
-                     "attn_jvp_proj", "attn_jvp_status_string", "attn_jvp_version"]
+                     "attn_jvp_proj", "attn_jvp_rmsnorm_rope", "attn_jvp_status_string", "attn_jvp_version"]
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert A.attn_jvp_version() == 10200
+    assert A.attn_jvp_version() == 10300
     assert A.attn_jvp_status_string(0) == "ok"
     assert A.attn_jvp_status_string(A.ATTN_JVP_EUNSUPPORTED).startswith("unsupported")
     assert A.attn_jvp_status_string(99) == "unknown status"
@@ -132,6 +132,7 @@ def test_ctypes_signature_is_c_abi(lib):
     assert len(lib.attn_jvp_fwd_part.argtypes) == 19
     assert len(lib.attn_jvp_merge.argtypes) == 13
     assert len(lib.attn_jvp_proj.argtypes) == 14
+    assert len(lib.attn_jvp_rmsnorm_rope.argtypes) == 14
 
 
 def test_merge_part_limit_matches_header():
@@ -300,3 +301,43 @@ def test_grids_just_below_2_24_workgroups_pass_host_checks(lib):
     assert call(B=1, H=(1 << 24) - 1, Lq=1, Lk=1, d=64) == A.ATTN_JVP_ELAUNCH
     assert call_merge(rows=((1 << 24) - 1) * 16, d=128) == A.ATTN_JVP_ELAUNCH
     assert call_proj(B=(1 << 24) - 1, L=1, n_out=1, H=2, d=128) == A.ATTN_JVP_ELAUNCH
+
+
+def call_nr(ptrs=None, B=1, H=2, L=8, d=64, eps=1e-6, dtype=1):
+    p = ptrs if ptrs is not None else [FAKE] * 7
+    return A.attn_jvp_rmsnorm_rope(*p, B, H, L, d, eps, dtype)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), A.ATTN_JVP_EINVAL),
+    (dict(L=-1), A.ATTN_JVP_EINVAL),
+    (dict(d=96), A.ATTN_JVP_EUNSUPPORTED),
+    (dict(eps=-1e-6), A.ATTN_JVP_EINVAL),
+    (dict(eps=float("nan")), A.ATTN_JVP_EINVAL),
+    (dict(eps=float("inf")), A.ATTN_JVP_EINVAL),
+    (dict(ptrs=[0] + [FAKE] * 6), A.ATTN_JVP_EINVAL),
+    (dict(ptrs=[FAKE] * 2 + [0] + [FAKE] * 4), A.ATTN_JVP_EINVAL),
+    (dict(ptrs=[FAKE, 0] + [FAKE] * 5), A.ATTN_JVP_EINVAL),
+    (dict(ptrs=[FAKE] * 5 + [0, FAKE]), A.ATTN_JVP_EINVAL),
+    (dict(ptrs=[FAKE + 8] + [FAKE] * 6), A.ATTN_JVP_EALIGN),
+    (dict(ptrs=[FAKE] * 4 + [FAKE + 2] + [FAKE] * 2), A.ATTN_JVP_EALIGN),
+    (dict(ptrs=[FAKE] * 6 + [FAKE + 4]), A.ATTN_JVP_EALIGN),
+    (dict(B=1 << 12, H=1 << 12), A.ATTN_JVP_EUNSUPPORTED),
+    (dict(H=1 << 20, L=1 << 10), A.ATTN_JVP_EUNSUPPORTED),
+    (dict(L=1 << 31), A.ATTN_JVP_EUNSUPPORTED),
+])
+def test_rmsnorm_rope_rejects_invalid_arguments(lib, kw, status):
+    assert call_nr(**kw) == status
+    assert A.attn_jvp_last_error() != ""
+
+
+def test_rmsnorm_rope_zero_size_and_optional_inputs(lib):
+    import torch
+
+    for kw in (dict(B=0), dict(H=0), dict(L=0)):
+        assert call_nr(ptrs=[0] * 7, **kw) == A.ATTN_JVP_OK
+    if torch.cuda.device_count() > 0:
+        return
+    # no tangent, no gain, no tables: every optional input may be NULL together
+    assert call_nr(ptrs=[FAKE, 0, FAKE, 0, 0, 0, 0]) == A.ATTN_JVP_ELAUNCH
+    assert call_nr(ptrs=[FAKE] * 7, dtype=0, d=128) == A.ATTN_JVP_ELAUNCH

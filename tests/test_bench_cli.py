@@ -94,3 +94,9 @@ def test_trace_summary_skips_warmups(tmp_path):
     assert "other" not in out["kernel_trace"]
     c = out["counters"]["k<a>"]
     assert c == [{"dispatch": 3, "X": 5.0, "_duration_ns": 20}]
+
+
+def test_norm_rope_workload_is_checked():
+    r = bench("--norm-rope", "nope")
+    assert r.returncode == 2
+    assert "q_video_bf16" in r.stderr

@@ -80,3 +80,11 @@ def test_default_bench_line_carries_every_workload():
         assert abs(e["tflops"] - e["flops_per_launch"] / (e["avg_launch_ms"] * 1e-3) / 1e12) < 1e-2 * e["tflops"]
     assert pw["tiny_self_fp32"]["peak"] == 157.3 and pw["image_self_bf16"]["peak"] == 2500.0
     assert pw["text_cross_bf16_frozen"]["flops_per_launch"] * 1.5 == pw["text_cross_bf16"]["flops_per_launch"]
+
+
+def test_norm_rope_bench_line():
+    d = bench("--norm-rope", "q_image_bf16", "--steps", "3", "--warmup", "1", "--cpu-budget", "1")
+    check_common(d, 3, 1, "q_image_bf16", "bf16")
+    assert d["roofline"]["bound"] == "hbm" and d["roofline"]["peak"] == 8000.0
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]

@@ -1,0 +1,169 @@
+"""GPU parity of the query/key RMS normalisation and rotary embedding with its
+tangent (attn_jvp_rmsnorm_rope), through the C ABI, against the fp64 oracle.
+
+Tolerance, from the arithmetic: each output is computed in fp32 (a sum of d
+squares and of d products for the row statistics, a reciprocal square root,
+two products per rotated element) and rounded once to the element type.  The
+fp32 part stays within 1e-5 of the tensor's largest value (about d ulps of the
+sums); bf16 rounding to nearest adds at most 2^-9 of the fp32 value, so per
+element |y - ref| <= 2^-8 |ref| + 2e-5 max|ref| for bf16 and
+|y - ref| <= 1e-5 max|ref| for fp32, the same for the tangent.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import norm_rope_jvp
+from workloads import NORM_ROPE_WORKLOADS, custom_norm_rope, norm_rope_array, rope_tables
+from workloads.device import device_norm_rope_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def A():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_forward_mode_attn_amd as A
+
+    A.load_library()
+    return A
+
+
+def oracle_head(w, b, h, rows=None, x_override=None):
+    x = norm_rope_array(w, "x", b, h) if x_override is None else x_override
+    tx = norm_rope_array(w, "tx", b, h) if w.tangent else None
+    g = norm_rope_array(w, "gamma") if w.gain else None
+    c, s = rope_tables(w)
+    if rows is not None:
+        x = x[rows]
+        tx = tx[rows] if tx is not None else None
+        c = c[rows] if c is not None else None
+        s = s[rows] if s is not None else None
+    return norm_rope_jvp(x, tx, g, c, s, w.eps)
+
+
+def within(got, ref, dtype):
+    got = np.asarray(got, dtype=np.float64)
+    big = float(np.max(np.abs(ref))) if ref.size else 0.0
+    bound = (2.0 ** -8 * np.abs(ref) + 2e-5 * big) if dtype == "bf16" else np.full(ref.shape, 1e-5 * big)
+    err = np.abs(got - ref)
+    return bool(np.all(err <= bound)), float(np.max(err / np.maximum(bound, 1e-300))) if ref.size else 0.0
+
+
+def check(w, y, ty, heads=None, rows_fn=None, x_override=None):
+    worst = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            if heads is not None and (b, h) not in heads:
+                continue
+            rows = rows_fn(b, h) if rows_fn else None
+            Y, TY = oracle_head(w, b, h, rows, None if x_override is None else x_override.get((b, h)))
+            gy = y[b, h].float().cpu().numpy()
+            gy = gy[rows] if rows is not None else gy
+            ok, r = within(gy, Y, w.dtype)
+            assert ok, f"{w.name} y (b={b}, h={h}): worst error/bound {r:.3f}"
+            worst = max(worst, r)
+            if w.tangent:
+                gt = ty[b, h].float().cpu().numpy()
+                gt = gt[rows] if rows is not None else gt
+                ok, r = within(gt, TY, w.dtype)
+                assert ok, f"{w.name} ty (b={b}, h={h}): worst error/bound {r:.3f}"
+                worst = max(worst, r)
+    print(f"  {w.name} B{w.B} H{w.H} L{w.L} d{w.d} {w.dtype}: worst error/bound {worst:.3f}", flush=True)
+
+
+SHAPES = [
+    # (B, H, L, d, dtype, tangent, rope, gain)
+    (1, 1, 1, 64, "bf16", True, True, True),
+    (1, 2, 7, 128, "bf16", True, True, True),
+    (2, 3, 17, 64, "bf16", True, False, True),
+    (1, 2, 33, 128, "bf16", False, True, False),
+    (2, 2, 257, 128, "bf16", True, True, True),
+    (1, 1, 16, 128, "fp32", True, True, True),
+    (1, 3, 9, 128, "fp32", True, True, False),
+    (2, 2, 100, 64, "fp32", True, True, True),
+    (1, 2, 31, 64, "fp32", False, False, True),
+]
+
+
+@pytest.mark.parametrize("B,H,L,d,dtype,tangent,rope,gain", SHAPES)
+def test_matches_oracle(A, B, H, L, d, dtype, tangent, rope, gain):
+    w = custom_norm_rope(B, H, L, d, dtype=dtype, tangent=tangent, rope=rope, gain=gain,
+                         seed_id=3100 + L * 3 + d + (7 if dtype == "fp32" else 0))
+    print(f"case norm_rope B{B} H{H} L{L} d{d} {dtype} tangent={tangent} rope={rope} gain={gain}", flush=True)
+    x = device_norm_rope_inputs(w)
+    # outputs with guard bands: the kernel must write exactly the [B, H, L, d] extent
+    n = w.B * w.H * w.L * w.d
+    gy = torch.full((n + 64,), float("nan"), dtype=x["x"].dtype, device=x["x"].device)
+    gty = torch.full((n + 64,), float("nan"), dtype=x["x"].dtype, device=x["x"].device)
+    y = gy[32:32 + n].view(w.shape())
+    ty = gty[32:32 + n].view(w.shape()) if tangent else None
+    A.rmsnorm_rope(x["x"], x["tx"], x["gamma"], x["cos"], x["sin"], eps=w.eps, out=(y, ty))
+    torch.cuda.synchronize()
+    assert torch.isnan(gy[:32].float()).all() and torch.isnan(gy[32 + n:].float()).all()
+    if tangent:
+        assert torch.isnan(gty[:32].float()).all() and torch.isnan(gty[32 + n:].float()).all()
+    check(w, y, ty)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_in_place_equals_out_of_place(A, dtype):
+    w = custom_norm_rope(2, 2, 130, 128, dtype=dtype, seed_id=3300)
+    print(f"case norm_rope in place {dtype}", flush=True)
+    x = device_norm_rope_inputs(w)
+    y, ty = A.rmsnorm_rope(x["x"], x["tx"], x["gamma"], x["cos"], x["sin"], eps=w.eps)
+    xi, txi = x["x"].clone(), x["tx"].clone()
+    y2, ty2 = A.rmsnorm_rope(xi, txi, x["gamma"], x["cos"], x["sin"], eps=w.eps, inplace=True)
+    torch.cuda.synchronize()
+    assert y2.data_ptr() == xi.data_ptr() and ty2.data_ptr() == txi.data_ptr()
+    assert torch.equal(y, xi) and torch.equal(ty, txi)
+
+
+def test_zero_row_with_eps(A):
+    """A row of zeros with eps > 0 normalises to zeros, and its tangent to g*tx/sqrt(eps)."""
+    w = custom_norm_rope(1, 2, 20, 64, dtype="fp32", eps=1e-3, seed_id=3400)
+    print("case norm_rope zero row", flush=True)
+    x = device_norm_rope_inputs(w)
+    x["x"][0, 1, 5].zero_()
+    y, ty = A.rmsnorm_rope(x["x"], x["tx"], x["gamma"], x["cos"], x["sin"], eps=w.eps)
+    torch.cuda.synchronize()
+    xo = norm_rope_array(w, "x", 0, 1).copy()
+    xo[5] = 0.0
+    check(w, y, ty, x_override={(0, 1): xo})
+    assert float(y[0, 1, 5].abs().max()) == 0.0
+
+
+def test_image_queries(A):
+    w = NORM_ROPE_WORKLOADS["q_image_bf16"]
+    print(f"case {w.name}", flush=True)
+    x = device_norm_rope_inputs(w)
+    y, ty = A.rmsnorm_rope(x["x"], x["tx"], x["gamma"], x["cos"], x["sin"], eps=w.eps)
+    torch.cuda.synchronize()
+    check(w, y, ty)
+
+
+def test_text_keys_without_tangent(A):
+    w = NORM_ROPE_WORKLOADS["k_text_frozen_bf16"]
+    print(f"case {w.name}", flush=True)
+    x = device_norm_rope_inputs(w)
+    y, ty = A.rmsnorm_rope(x["x"], None, x["gamma"], None, None, eps=w.eps)
+    torch.cuda.synchronize()
+    assert ty is None
+    check(w, y, None)
+
+
+def test_video_queries_sampled(A):
+    """The full video layer (40 heads x 32760 rows) in the launch the bench
+    times; checked on 512 seeded rows per head, both ends included."""
+    w = NORM_ROPE_WORKLOADS["q_video_bf16"]
+    print(f"case {w.name} (sampled rows)", flush=True)
+    x = device_norm_rope_inputs(w)
+    y, ty = A.rmsnorm_rope(x["x"], x["tx"], x["gamma"], x["cos"], x["sin"], eps=w.eps)
+    torch.cuda.synchronize()
+
+    def rows(b, h):
+        r = np.random.default_rng(1000 + h).choice(w.L, 500, replace=False)
+        return np.unique(np.concatenate([r, np.arange(6), np.arange(w.L - 6, w.L)]))
+
+    check(w, y, ty, rows_fn=rows)
