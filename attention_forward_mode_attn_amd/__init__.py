@@ -15,14 +15,14 @@ import ctypes
 import os
 
 __all__ = [
-    "ATTN_JVP_FP32", "ATTN_JVP_BF16", "ATTN_JVP_OK", "ATTN_JVP_EINVAL", "ATTN_JVP_EUNSUPPORTED",
+    "ATTN_JVP_FP32", "ATTN_JVP_BF16", "ATTN_JVP_BF16_F32OUT", "ATTN_JVP_OK", "ATTN_JVP_EINVAL", "ATTN_JVP_EUNSUPPORTED",
     "ATTN_JVP_EALIGN", "ATTN_JVP_ELAUNCH", "ATTN_JVP_MAX_MERGE_PARTS", "AttnJvpError", "attn_jvp_fwd",
     "attn_jvp_fwd_part", "attn_jvp_merge", "attn_jvp_status_string", "attn_jvp_last_error",
     "attn_jvp_version", "attn_jvp_proj", "attn_jvp_rmsnorm_rope", "fwd", "fwd_part", "merge", "fwd_split",
     "shard_bounds", "proj", "rmsnorm_rope", "library_path", "load_library",
 ]
 
-ATTN_JVP_FP32, ATTN_JVP_BF16 = 0, 1
+ATTN_JVP_FP32, ATTN_JVP_BF16, ATTN_JVP_BF16_F32OUT = 0, 1, 2
 ATTN_JVP_OK, ATTN_JVP_EINVAL, ATTN_JVP_EUNSUPPORTED, ATTN_JVP_EALIGN, ATTN_JVP_ELAUNCH = 0, 1, 2, 3, 4
 ATTN_JVP_MAX_MERGE_PARTS = 16
 
@@ -153,27 +153,40 @@ def attn_jvp_version() -> int:
     return int(load_library().attn_jvp_version())
 
 
-def fwd(q, k, v, tq, tk, tv, scale=None, out=None, stream=None):
+def _out_dtype(q, f32_out):
+    """The C dtype code and torch dtype of O and tO: the inputs' own, or float32
+    for bfloat16 inputs when ``f32_out`` (ATTN_JVP_BF16_F32OUT)."""
+    import torch
+
+    if not f32_out or q.dtype == torch.float32:
+        return None, q.dtype
+    return ATTN_JVP_BF16_F32OUT, torch.float32
+
+
+def fwd(q, k, v, tq, tk, tv, scale=None, out=None, stream=None, f32_out=False):
     """O, tO, lse for torch tensors q, tq [B,H,Lq,d] and k, v, tk, tv [B,H,Lk,d]
     (contiguous, same device, all float32 or all bfloat16); tk = tv = None is
     a frozen context (zero key-side tangents, computed without them).  Outputs are
-    allocated unless ``out=(o, to, lse)`` is given.  Runs on ``stream`` (a
-    torch.cuda.Stream) or the current stream."""
+    allocated unless ``out=(o, to, lse)`` is given; with ``f32_out`` bfloat16
+    inputs give float32 O and tO.  Runs on ``stream`` (a torch.cuda.Stream) or the
+    current stream."""
     import torch
 
     dtype = _check_inputs(q, k, v, tq, tk, tv)
+    code, odt = _out_dtype(q, f32_out)
+    dtype = code if code is not None else dtype
     B, H, Lq, d = q.shape
     Lk = k.shape[2]
     if scale is None:
         scale = d ** -0.5
     if out is None:
-        o = torch.empty_like(q)
-        to = torch.empty_like(q)
+        o = torch.empty(q.shape, dtype=odt, device=q.device)
+        to = torch.empty(q.shape, dtype=odt, device=q.device)
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
     else:
         o, to, lse = out
-        _check_out(o, q.shape, q.dtype, q.device, "o")
-        _check_out(to, q.shape, q.dtype, q.device, "to")
+        _check_out(o, q.shape, odt, q.device, "o")
+        _check_out(to, q.shape, odt, q.device, "to")
         _check_out(lse, (B, H, Lq), torch.float32, q.device, "lse")
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):  # launch on the inputs' device
@@ -213,13 +226,17 @@ def _check_inputs(q, k, v, tq, tk, tv):
     return ATTN_JVP_BF16 if dt == torch.bfloat16 else ATTN_JVP_FP32
 
 
-def fwd_part(q, k, v, tq, tk, tv, k0, k1, scale=None, out=None, stream=None):
+def fwd_part(q, k, v, tq, tk, tv, k0, k1, scale=None, out=None, stream=None, f32_out=False):
     """O, tO, lse, tlse of the keys [k0, k1) of k, v, tk, tv (torch tensors as
     in ``fwd``): the partial result of one key shard.  The shard is addressed
-    in place (no copy).  ``out=(o, to, lse, tlse)`` reuses buffers."""
+    in place (no copy).  ``out=(o, to, lse, tlse)`` reuses buffers; with
+    ``f32_out`` bfloat16 inputs give float32 partial O and tO, which ``merge``
+    rounds to bfloat16 once."""
     import torch
 
     dtype = _check_inputs(q, k, v, tq, tk, tv)
+    code, odt = _out_dtype(q, f32_out)
+    dtype = code if code is not None else dtype
     B, H, Lq, d = q.shape
     Lk = k.shape[2]
     if not 0 <= k0 < k1 <= Lk:
@@ -227,13 +244,14 @@ def fwd_part(q, k, v, tq, tk, tv, k0, k1, scale=None, out=None, stream=None):
     if scale is None:
         scale = d ** -0.5
     if out is None:
-        o, to = torch.empty_like(q), torch.empty_like(q)
+        o = torch.empty(q.shape, dtype=odt, device=q.device)
+        to = torch.empty(q.shape, dtype=odt, device=q.device)
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
         tlse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
     else:
         o, to, lse, tlse = out
-        _check_out(o, q.shape, q.dtype, q.device, "o")
-        _check_out(to, q.shape, q.dtype, q.device, "to")
+        _check_out(o, q.shape, odt, q.device, "o")
+        _check_out(to, q.shape, odt, q.device, "to")
         _check_out(lse, (B, H, Lq), torch.float32, q.device, "lse")
         _check_out(tlse, (B, H, Lq), torch.float32, q.device, "tlse")
     off = k0 * d * k.element_size()
@@ -248,9 +266,11 @@ def fwd_part(q, k, v, tq, tk, tv, k0, k1, scale=None, out=None, stream=None):
     return o, to, lse, tlse
 
 
-def merge(parts, out=None, stream=None):
+def merge(parts, out=None, stream=None, out_dtype=None):
     """Exact merge of partial results ``parts`` = [(o, to, lse, tlse), ...]
-    over disjoint key shards; returns (o, to, lse, tlse) of the union."""
+    over disjoint key shards; returns (o, to, lse, tlse) of the union.  The
+    result has the parts' dtype, or bfloat16 for float32 parts with
+    ``out_dtype=torch.bfloat16``."""
     import torch
 
     if not 1 <= len(parts) <= ATTN_JVP_MAX_MERGE_PARTS:
@@ -261,6 +281,11 @@ def merge(parts, out=None, stream=None):
     if o0.device.type != "cuda":
         raise ValueError("parts must be GPU tensors")
     dtype = ATTN_JVP_BF16 if o0.dtype == torch.bfloat16 else ATTN_JVP_FP32
+    odt = o0.dtype if out_dtype is None else out_dtype
+    if odt != o0.dtype:
+        if not (o0.dtype == torch.float32 and odt == torch.bfloat16):
+            raise ValueError("out_dtype: bfloat16 from float32 parts is the one conversion the merge makes")
+        dtype = ATTN_JVP_BF16_F32OUT
     d = o0.shape[-1]
     rows = o0.numel() // d
     for o, to, lse, tlse in parts:
@@ -273,12 +298,13 @@ def merge(parts, out=None, stream=None):
         if any(x.device != o0.device for x in (o, to, lse, tlse)):
             raise ValueError("all parts on one device")
     if out is None:
-        o, to = torch.empty_like(o0), torch.empty_like(o0)
+        o = torch.empty(o0.shape, dtype=odt, device=o0.device)
+        to = torch.empty(o0.shape, dtype=odt, device=o0.device)
         lse, tlse = torch.empty_like(parts[0][2]), torch.empty_like(parts[0][3])
     else:
         o, to, lse, tlse = out
-        _check_out(o, o0.shape, o0.dtype, o0.device, "o")
-        _check_out(to, o0.shape, o0.dtype, o0.device, "to")
+        _check_out(o, o0.shape, odt, o0.device, "o")
+        _check_out(to, o0.shape, odt, o0.device, "to")
         _check_out(lse, parts[0][2].shape, torch.float32, o0.device, "lse")
         _check_out(tlse, parts[0][2].shape, torch.float32, o0.device, "tlse")
     s = stream if stream is not None else torch.cuda.current_stream(o0.device)
@@ -303,12 +329,14 @@ def shard_bounds(Lk: int, n: int, align: int = 64):
     return [(cuts[i], cuts[i + 1]) for i in range(n)]
 
 
-def fwd_split(q, k, v, tq, tk, tv, n_split, scale=None, stream=None):
+def fwd_split(q, k, v, tq, tk, tv, n_split, scale=None, stream=None, f32_partials=False):
     """The attention-JVP computed as ``n_split`` key shards and merged:
-    returns (o, to, lse, tlse), equal to ``fwd`` (plus tlse) up to rounding."""
-    parts = [fwd_part(q, k, v, tq, tk, tv, a, b, scale=scale, stream=stream)
+    returns (o, to, lse, tlse), equal to ``fwd`` (plus tlse) up to rounding.
+    With ``f32_partials`` bfloat16 shards are kept in float32 and the result is
+    rounded to bfloat16 once, by the merge."""
+    parts = [fwd_part(q, k, v, tq, tk, tv, a, b, scale=scale, stream=stream, f32_out=f32_partials)
              for a, b in shard_bounds(k.shape[2], n_split)]
-    return merge(parts, stream=stream)
+    return merge(parts, stream=stream, out_dtype=q.dtype)
 
 
 def proj(x, tx, w, bias=None, n_out=3, heads=None, out=None, stream=None):

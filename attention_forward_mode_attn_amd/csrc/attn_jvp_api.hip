@@ -53,7 +53,8 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* tq, const 
              void* to, float* lse, float* tlse, int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t kv_rows,
              int64_t d, float scale, int dtype, void* stream) {
   g_last_error[0] = '\0';
-  if (dtype != ATTN_JVP_FP32 && dtype != ATTN_JVP_BF16) return fail(ATTN_JVP_EINVAL, "dtype must be 0 (fp32) or 1 (bf16)");
+  if (dtype != ATTN_JVP_FP32 && dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_BF16_F32OUT)
+    return fail(ATTN_JVP_EINVAL, "dtype must be 0 (fp32), 1 (bf16) or 2 (bf16 in, fp32 out)");
   if (B < 0 || H < 0 || Lq < 0 || Lk < 0 || d < 0) return fail(ATTN_JVP_EINVAL, "negative size");
   if (d != 64 && d != 128) return fail(ATTN_JVP_EUNSUPPORTED, "head dimension must be 64 or 128");
   if (B == 0 || H == 0 || Lq == 0) return ATTN_JVP_OK;  // nothing to compute
@@ -79,8 +80,9 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* tq, const 
   p.B = (int)B; p.H = (int)H; p.Lq = (int)Lq; p.Lk = (int)Lk; p.d = (int)d;
   p.kv_rows = (int)kv_rows;
   p.scale = scale;
+  p.out_f32 = dtype == ATTN_JVP_BF16_F32OUT;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const hipError_t e = dtype == ATTN_JVP_BF16 ? attnjvp::launch_bf16(p, s) : attnjvp::launch_fp32(p, s);
+  const hipError_t e = dtype == ATTN_JVP_FP32 ? attnjvp::launch_fp32(p, s) : attnjvp::launch_bf16(p, s);
   if (e != hipSuccess) {
     std::snprintf(g_last_error, sizeof g_last_error, "HIP error %d: %s", (int)e, hipGetErrorString(e));
     return ATTN_JVP_ELAUNCH;
@@ -109,7 +111,8 @@ int attn_jvp_merge(int n, const void* const* o_parts, const void* const* to_part
                    const float* const* tlse_parts, void* o, void* to, float* lse, float* tlse, int64_t rows,
                    int64_t d, int dtype, void* stream) {
   g_last_error[0] = '\0';
-  if (dtype != ATTN_JVP_FP32 && dtype != ATTN_JVP_BF16) return fail(ATTN_JVP_EINVAL, "dtype must be 0 (fp32) or 1 (bf16)");
+  if (dtype != ATTN_JVP_FP32 && dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_BF16_F32OUT)
+    return fail(ATTN_JVP_EINVAL, "dtype must be 0 (fp32), 1 (bf16) or 2 (fp32 parts, bf16 result)");
   if (n < 1 || n > ATTN_JVP_MAX_MERGE_PARTS) return fail(ATTN_JVP_EINVAL, "n must be in 1 .. ATTN_JVP_MAX_MERGE_PARTS");
   if (rows < 0 || d < 0) return fail(ATTN_JVP_EINVAL, "negative size");
   if (d != 64 && d != 128) return fail(ATTN_JVP_EUNSUPPORTED, "head dimension must be 64 or 128");
@@ -140,7 +143,8 @@ int attn_jvp_merge(int n, const void* const* o_parts, const void* const* to_part
   p.out_tlse = tlse;
   p.rows = rows;
   p.d = (int)d;
-  p.bf16 = dtype == ATTN_JVP_BF16;
+  p.in_bf16 = dtype == ATTN_JVP_BF16;
+  p.out_bf16 = dtype != ATTN_JVP_FP32;
   const hipError_t e = attnjvp::launch_merge(p, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     std::snprintf(g_last_error, sizeof g_last_error, "HIP error %d: %s", (int)e, hipGetErrorString(e));
@@ -152,7 +156,8 @@ int attn_jvp_merge(int n, const void* const* o_parts, const void* const* to_part
 int attn_jvp_proj(const void* x, const void* tx, const void* w, const void* bias, void* y, void* ty, int64_t B,
                   int64_t L, int64_t D, int64_t n_out, int64_t H, int64_t d, int dtype, void* stream) {
   g_last_error[0] = '\0';
-  if (dtype != ATTN_JVP_FP32 && dtype != ATTN_JVP_BF16) return fail(ATTN_JVP_EINVAL, "dtype must be 0 (fp32) or 1 (bf16)");
+  if (dtype != ATTN_JVP_FP32 && dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_BF16_F32OUT)
+    return fail(ATTN_JVP_EINVAL, "dtype must be 0 (fp32), 1 (bf16) or 2 (bf16 in, fp32 out)");
   if (B < 0 || L < 0 || D < 0 || n_out < 0 || H < 0 || d < 0) return fail(ATTN_JVP_EINVAL, "negative size");
   if (dtype != ATTN_JVP_BF16) return fail(ATTN_JVP_EUNSUPPORTED, "the projection is bf16 only");
   if (d != 64 && d != 128) return fail(ATTN_JVP_EUNSUPPORTED, "head dimension must be 64 or 128");
@@ -189,9 +194,11 @@ int attn_jvp_rmsnorm_rope(const void* x, const void* tx, void* y, void* ty, cons
                           const float* rope_sin, int64_t B, int64_t H, int64_t L, int64_t d, float eps, int dtype,
                           void* stream) {
   g_last_error[0] = '\0';
-  if (dtype != ATTN_JVP_FP32 && dtype != ATTN_JVP_BF16) return fail(ATTN_JVP_EINVAL, "dtype must be 0 (fp32) or 1 (bf16)");
+  if (dtype != ATTN_JVP_FP32 && dtype != ATTN_JVP_BF16 && dtype != ATTN_JVP_BF16_F32OUT)
+    return fail(ATTN_JVP_EINVAL, "dtype must be 0 (fp32), 1 (bf16) or 2 (bf16 in, fp32 out)");
   if (B < 0 || H < 0 || L < 0 || d < 0) return fail(ATTN_JVP_EINVAL, "negative size");
   if (d != 64 && d != 128) return fail(ATTN_JVP_EUNSUPPORTED, "head dimension must be 64 or 128");
+  if (dtype == ATTN_JVP_BF16_F32OUT) return fail(ATTN_JVP_EUNSUPPORTED, "float32 outputs apply to the attention outputs only");
   if (B == 0 || H == 0 || L == 0) return ATTN_JVP_OK;  // nothing to compute
   if (!std::isfinite(eps) || eps < 0.0f) return fail(ATTN_JVP_EINVAL, "eps must be finite and >= 0");
   if (!x || !y) return fail(ATTN_JVP_EINVAL, "NULL pointer");

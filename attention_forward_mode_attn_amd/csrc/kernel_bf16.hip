@@ -55,6 +55,7 @@ struct Params {
   float* tlse;
   int Lq, Lk, kv_rows, n_qtiles, n_blocks;
   float scale;
+  int out_f32;  // O and tO written as float32 (else bf16)
 };
 
 template <int D>
@@ -576,6 +577,33 @@ void attn_jvp_bf16_kernel(Params p) {
   // ---- epilogue ------------------------------------------------------------
   const float l = xhalf_sum(st.l), a = xhalf_sum(st.a);
   const float inv = 1.0f / l, mu = a * inv;
+  if (p.out_f32) {
+    // float32 O and tO (the partial results of a key shard, rounded to bf16
+    // only once, after the merge): group g of a lane is 4 consecutive dims,
+    // one 16-byte store each.
+    const auto ro32 = make_rsrc((const char*)p.o + 2 * qhead, 2 * qbytes);
+    const auto rto32 = make_rsrc((const char*)p.to + 2 * qhead, 2 * qbytes);
+    u32x4 o32[C::kBlocksD][4], t32[C::kBlocksD][4];
+#pragma unroll
+    for (int b = 0; b < C::kBlocksD; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = acc_o[b][4 * g + i];
+          o32[b][g][i] = __float_as_uint(x * inv);
+          t32[b][g][i] = __float_as_uint((acc_t[b][4 * g + i] - mu * x) * inv);
+        }
+    fence();
+    const uint32_t obase32 = ((uint32_t)qrow * D + 4 * hh) * 4;
+#pragma unroll
+    for (int b = 0; b < C::kBlocksD; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        __builtin_amdgcn_raw_buffer_store_b128(o32[b][g], ro32, obase32, (32 * b + 8 * g) * 4, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(t32[b][g], rto32, obase32, (32 * b + 8 * g) * 4, 0);
+      }
+  } else {
   const auto ro = make_rsrc((const char*)p.o + qhead, qbytes);
   const auto rto = make_rsrc((const char*)p.to + qhead, qbytes);
   // Accumulator group g (registers 4g..4g+3) of a lane holds head dims
@@ -620,6 +648,7 @@ void attn_jvp_bf16_kernel(Params p) {
       __builtin_amdgcn_raw_buffer_store_b128(ost[b][gp], ro, obase, (32 * b + 16 * gp) * 2, 0);
       __builtin_amdgcn_raw_buffer_store_b128(tst[b][gp], rto, obase, (32 * b + 16 * gp) * 2, 0);
     }
+  }
   if (hh == 0) {
     const auto rl = make_rsrc((const char*)p.lse + (size_t)bh * Lq * 4, (uint32_t)Lq * 4);
     buf_store4(rl, (uint32_t)qrow * 4, (st.m + __builtin_amdgcn_logf(l)) * kLn2);
@@ -636,6 +665,7 @@ hipError_t launch(const Problem& pr, hipStream_t stream) {
   p.q = pr.q; p.k = pr.k; p.v = pr.v; p.tq = pr.tq; p.tk = pr.tk; p.tv = pr.tv;
   p.o = pr.o; p.to = pr.to; p.lse = pr.lse; p.tlse = pr.tlse;
   p.Lq = pr.Lq; p.Lk = pr.Lk; p.kv_rows = pr.kv_rows; p.scale = pr.scale;
+  p.out_f32 = pr.out_f32 ? 1 : 0;
   p.n_qtiles = (pr.Lq + kBlockRows - 1) / kBlockRows;
   p.n_blocks = pr.B * pr.H * p.n_qtiles;
   return launch_1d(reinterpret_cast<const void*>(&attn_jvp_bf16_kernel<D, kFrozen>), p.n_blocks, kThreads, p, stream);

@@ -29,6 +29,7 @@ struct Problem {
   int B, H, Lq, Lk, d;
   int kv_rows;  // rows between consecutive K/V heads in memory (>= Lk)
   float scale;
+  bool out_f32;  // bf16 inputs: O and tO written as float32 instead of bf16
 };
 
 // Both assume validated arguments (see the C ABI) and B*H*Lq > 0, Lk > 0.
@@ -49,7 +50,8 @@ struct MergeProblem {
   float* out_tlse;  // may be null
   int64_t rows;     // > 0
   int d;            // 64 or 128
-  bool bf16;
+  bool in_bf16;     // partial O, tO in bf16 (else float32)
+  bool out_bf16;    // merged O, tO in bf16 (else float32)
 };
 
 hipError_t launch_merge(const MergeProblem& p, hipStream_t stream);

@@ -17,7 +17,12 @@
 //
 // The merge is bound by memory traffic: each thread merges 8 consecutive
 // elements of one row (16-byte bf16 / 32-byte fp32 accesses), the row's
-// weights recomputed per thread from the n scalars.
+// weights recomputed per thread from the n scalars in one pass with a running
+// maximum.  The first part's data are requested before that pass and each
+// next part's during the current part's arithmetic, so every thread keeps a
+// part in flight (66-68 VGPRs: 7 waves per SIMD).  Partials are bf16 or
+// float32 (a bf16 pass can write float32 partials, so that the result is
+// rounded to bf16 once, here); the result is bf16 or float32.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -70,7 +75,7 @@ __device__ inline void store8(void* base, size_t elem, const float (&x)[8]) {
   }
 }
 
-template <bool BF16, int D>
+template <bool kInBF16, bool kOutBF16, int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs args) {
   const MergeProblem& p = args.p;
   constexpr int kThreadsPerRow = D / 8;
@@ -79,50 +84,70 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs args) {
   if (row >= p.rows) return;
   const int col = (threadIdx.x % kThreadsPerRow) * 8;
   const int n = p.n;
-
-  float lmax = -INFINITY;
-  for (int s = 0; s < n; ++s) lmax = fmaxf(lmax, p.lse[s][row]);
-  float wsum = 0.0f;
-  for (int s = 0; s < n; ++s) wsum += expf(p.lse[s][row] - lmax);
-  const float inv = 1.0f / wsum;
-  float mu = 0.0f;
-  for (int s = 0; s < n; ++s) mu += expf(p.lse[s][row] - lmax) * inv * p.tlse[s][row];
-
   const size_t elem = (size_t)row * D + col;
+
+  // part 0's data in flight while the row's weights are computed
+  float os[8], ts[8];
+  load8<kInBF16>(p.o[0], elem, os);
+  load8<kInBF16>(p.to[0], elem, ts);
+
+  // one pass over the n (lse, tlse) pairs with a running maximum
+  float lmax = -INFINITY, wsum = 0.0f, mun = 0.0f;
+  for (int s = 0; s < n; ++s) {
+    const float l = p.lse[s][row], t = p.tlse[s][row];
+    const float m = fmaxf(lmax, l);
+    const float r = expf(lmax - m), e = expf(l - m);
+    wsum = wsum * r + e;
+    mun = mun * r + e * t;
+    lmax = m;
+  }
+  const float inv = 1.0f / wsum, mu = mun * inv;
+
   float o[8] = {}, to[8] = {};
   for (int s = 0; s < n; ++s) {
+    float on[8], tn[8];
+    if (s + 1 < n) {  // the next part's data in flight under this part's arithmetic
+      load8<kInBF16>(p.o[s + 1], elem, on);
+      load8<kInBF16>(p.to[s + 1], elem, tn);
+    }
     const float w = expf(p.lse[s][row] - lmax) * inv;
     const float shift = p.tlse[s][row] - mu;
-    float os[8], ts[8];
-    load8<BF16>(p.o[s], elem, os);
-    load8<BF16>(p.to[s], elem, ts);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       o[i] += w * os[i];
       to[i] += w * (ts[i] + shift * os[i]);
     }
+    if (s + 1 < n) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        os[i] = on[i];
+        ts[i] = tn[i];
+      }
+    }
   }
-  store8<BF16>(p.out_o, elem, o);
-  store8<BF16>(p.out_to, elem, to);
+  store8<kOutBF16>(p.out_o, elem, o);
+  store8<kOutBF16>(p.out_to, elem, to);
   if (col == 0) {
     p.out_lse[row] = lmax + logf(wsum);
     if (p.out_tlse) p.out_tlse[row] = mu;
   }
 }
 
-template <bool BF16, int D>
+template <bool kInBF16, bool kOutBF16, int D>
 hipError_t launch(const MergeProblem& p, hipStream_t stream) {
   constexpr int kRowsPerBlock = 256 / (D / 8);
   const int64_t blocks = (p.rows + kRowsPerBlock - 1) / kRowsPerBlock;
   MergeArgs a{p};
-  return launch_1d(reinterpret_cast<const void*>(&merge_kernel<BF16, D>), (unsigned)blocks, 256, a, stream);
+  return launch_1d(reinterpret_cast<const void*>(&merge_kernel<kInBF16, kOutBF16, D>), (unsigned)blocks, 256, a,
+                   stream);
 }
 
 }  // namespace
 
 hipError_t launch_merge(const MergeProblem& p, hipStream_t stream) {
-  if (p.bf16) return p.d == 128 ? launch<true, 128>(p, stream) : launch<true, 64>(p, stream);
-  return p.d == 128 ? launch<false, 128>(p, stream) : launch<false, 64>(p, stream);
+  if (p.in_bf16) return p.d == 128 ? launch<true, true, 128>(p, stream) : launch<true, true, 64>(p, stream);
+  if (p.out_bf16) return p.d == 128 ? launch<false, true, 128>(p, stream) : launch<false, true, 64>(p, stream);
+  return p.d == 128 ? launch<false, false, 128>(p, stream) : launch<false, false, 64>(p, stream);
 }
 
 }  // namespace attnjvp

@@ -539,6 +539,9 @@ def main():
     ap.add_argument("--split", type=int, default=0,
                     help="time the key-sharded path: N attn_jvp_fwd_part passes plus attn_jvp_merge; "
                          "the roofline object then covers the merge launch (HBM bound)")
+    ap.add_argument("--f32-partials", action="store_true",
+                    help="with --split: bf16 shards write float32 partial O and tO (dtype 2), which the merge "
+                         "rounds to bf16 once")
     ap.add_argument("--frozen-context", action="store_true",
                     help="pass tk = tv = NULL (workloads whose key tangents are zero); "
                          "value is then executed TFLOP/s at 8 flops per logit and head dim")
@@ -623,8 +626,9 @@ def main():
     tk, tv = (None, None) if args.frozen_context else (x["tk"], x["tv"])
     if args.split:
         bounds = A.shard_bounds(w.Lk, args.split)
-        parts = [(torch.empty_like(o), torch.empty_like(o), torch.empty_like(lse), torch.empty_like(lse))
-                 for _ in bounds]
+        pdt = torch.float32 if args.f32_partials else o.dtype
+        parts = [(torch.empty(o.shape, dtype=pdt, device=dev), torch.empty(o.shape, dtype=pdt, device=dev),
+                  torch.empty_like(lse), torch.empty_like(lse)) for _ in bounds]
         tlse = torch.empty_like(lse)
         merge_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                     for _ in range(args.warmup + args.steps)]
@@ -635,11 +639,12 @@ def main():
             A.fwd(x["q"], x["k"], x["v"], x["tq"], tk, tv, scale=w.scale, out=(o, to, lse), stream=stream)
             return
         for (k0, k1), part in zip(bounds, parts):
-            A.fwd_part(x["q"], x["k"], x["v"], x["tq"], tk, tv, k0, k1, scale=w.scale, out=part, stream=stream)
+            A.fwd_part(x["q"], x["k"], x["v"], x["tq"], tk, tv, k0, k1, scale=w.scale, out=part, stream=stream,
+                       f32_out=args.f32_partials)
         a, b = merge_ev[n_step[0]]
         n_step[0] += 1
         a.record(stream)
-        A.merge(parts, out=(o, to, lse, tlse), stream=stream)
+        A.merge(parts, out=(o, to, lse, tlse), stream=stream, out_dtype=o.dtype)
         b.record(stream)
 
     for _ in range(args.warmup):
@@ -675,8 +680,8 @@ def main():
         merge_ms = sorted(a.elapsed_time(b) for a, b in timed)
         avg_merge_ms = sum(merge_ms) / len(merge_ms)
         rows = w.B * w.H * w.Lq
-        row_bytes = 2 * w.d * w.elem_bytes + 8
-        merge_bytes = float(rows * row_bytes * (len(bounds) + 1))
+        part_bytes = 2 * w.d * (4 if args.f32_partials else w.elem_bytes) + 8
+        merge_bytes = float(rows * (part_bytes * len(bounds) + 2 * w.d * w.elem_bytes + 8))
         roofline = {
             "bound": "hbm",
             "achieved": round(merge_bytes / (avg_merge_ms * 1e-3) / 1e9, 1),
@@ -684,7 +689,8 @@ def main():
             "unit": "GB/s",
             "frac": round(merge_bytes / (avg_merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "traffic": None,
-            "kernel": f"merge_kernel<{str(w.dtype == 'bf16').lower()}, {w.d}>",
+            "kernel": (f"merge_kernel<{str(w.dtype == 'bf16' and not args.f32_partials).lower()}, "
+                       f"{str(w.dtype == 'bf16').lower()}, {w.d}>"),
             "avg_launch_ms": round(avg_merge_ms, 4),
             "median_launch_ms": round(merge_ms[len(merge_ms) // 2], 4),
             "min_launch_ms": round(merge_ms[0], 4),
@@ -724,7 +730,8 @@ def main():
                    "scale": w.scale, "parallelism": "single GPU",
                    "path": ("frozen context (tk = tv = NULL; 8 executed flops per logit and head dim)"
                             if args.frozen_context else "full JVP (12 flops per logit and head dim)")
-                   + (f"; {args.split} key shards + exact merge" if args.split else "")},
+                   + (f"; {args.split} key shards + exact merge" if args.split else "")
+                   + ("; float32 partials" if args.split and args.f32_partials else "")},
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "wall_s_timed_region": round(wall, 3),
         "sclk_mhz": sclk,

@@ -34,16 +34,23 @@
 extern "C" {
 #endif
 
-#define ATTN_JVP_VERSION 10300 /* 1.3.0 */
+#define ATTN_JVP_VERSION 10400 /* 1.4.0 */
 
 /* Largest number of partial results one attn_jvp_merge call combines. */
 #define ATTN_JVP_MAX_MERGE_PARTS 16
 
 /* Element type of q, k, v, tq, tk, tv, o and to (lse is always float32). */
 typedef enum {
-  ATTN_JVP_FP32 = 0, /* float32 in, float32 out, float32 arithmetic */
-  ATTN_JVP_BF16 = 1  /* bfloat16 in, bfloat16 out (round to nearest even),
-                        bf16 matrix products with float32 accumulation */
+  ATTN_JVP_FP32 = 0,        /* float32 in, float32 out, float32 arithmetic */
+  ATTN_JVP_BF16 = 1,        /* bfloat16 in, bfloat16 out (round to nearest even),
+                               bf16 matrix products with float32 accumulation */
+  ATTN_JVP_BF16_F32OUT = 2  /* bfloat16 inputs as ATTN_JVP_BF16, o and to written as
+                               float32 (attn_jvp_fwd, attn_jvp_fwd_part); for
+                               attn_jvp_merge: float32 partials, bfloat16 result.
+                               Key-shard partials kept in float32 are rounded to
+                               bf16 once, after the merge.  Not accepted by
+                               attn_jvp_proj or attn_jvp_rmsnorm_rope
+                               (ATTN_JVP_EUNSUPPORTED). */
 } attn_jvp_dtype_t;
 
 typedef enum {
@@ -68,7 +75,8 @@ typedef enum {
  *           designs" item 1).  The bf16 path then skips the tK and tV
  *           products and copies (8 instead of 12 flops per logit and head
  *           dim); the result equals passing zero-filled tk, tv.
- *   o, to   [B, H, Lq, d]  outputs: attention output and its tangent (device, written)
+ *   o, to   [B, H, Lq, d]  outputs: attention output and its tangent (device, written),
+ *                          float32 for ATTN_JVP_BF16_F32OUT
  *   lse     [B, H, Lq]     float32 row log-sum-exp of scale*QK^T     (device, written)
  *   B, H, Lq, Lk, d        sizes; d in {64, 128}
  *   scale                  logit scale (usually 1/sqrt(d)); finite and > 0
@@ -148,12 +156,15 @@ int attn_jvp_fwd_part(const void* q, const void* k, const void* v,
  * Arguments
  *   n                      number of shards, 1 .. ATTN_JVP_MAX_MERGE_PARTS
  *   o_parts, to_parts      host arrays of n device pointers, [rows, d] each, dtype
+ *                          (float32 for ATTN_JVP_BF16_F32OUT, whose result is bf16)
  *   lse_parts, tlse_parts  host arrays of n device pointers, [rows] float32 each
  *   o, to                  [rows, d] outputs (device, written)
  *   lse                    [rows] float32 output (device, written)
  *   tlse                   [rows] float32 output, may be NULL (then not written)
  *   rows, d                d in {64, 128}
- *   dtype, stream          as attn_jvp_fwd (arithmetic is float32)
+ *   dtype, stream          as attn_jvp_fwd (arithmetic is float32): FP32 parts give an
+ *                          FP32 result, BF16 parts a BF16 result, BF16_F32OUT float32
+ *                          parts a BF16 result
  * Ownership, alignment (16 bytes for [rows, d] tensors, 4 for [rows]),
  * execution and errors follow attn_jvp_fwd; rows == 0 is a no-op; outputs must
  * not overlap any input.  The host arrays are read during the call only.

@@ -99,6 +99,14 @@ int main() {
         stub::last_problem.Lk == 7 && stub::last_problem.tlse == F(A0 + 144));
   CHECK(merge(16, 1000, 64) == ATTN_JVP_OK && stub::last_kind == stub::Kind::merge &&
         stub::last_merge.n == 16 && stub::last_merge.rows == 1000 && stub::last_merge.d == 64);
+  CHECK(stub::last_merge.in_bf16 && stub::last_merge.out_bf16);
+  CHECK(merge(3, 10, 128, 2) == ATTN_JVP_OK && !stub::last_merge.in_bf16 && stub::last_merge.out_bf16);
+  CHECK(merge(3, 10, 128, 0) == ATTN_JVP_OK && !stub::last_merge.in_bf16 && !stub::last_merge.out_bf16);
+  CHECK(fwd(1, 2, 10, 10, 64, 0.1f, 2) == ATTN_JVP_OK && stub::last_kind == stub::Kind::bf16 &&
+        stub::last_problem.out_f32);
+  CHECK(fwd(1, 2, 10, 10, 64, 0.1f, 1) == ATTN_JVP_OK && !stub::last_problem.out_f32);
+  CHECK(fwd(1, 2, 10, 10, 64, 0.1f, 3) == ATTN_JVP_EINVAL);
+  CHECK(norm_rope(1, 1, 8, 64, 0.0f, 2) == ATTN_JVP_EUNSUPPORTED);
   CHECK(proj(2, 100, 256, 3, 4, 64) == ATTN_JVP_OK && stub::last_kind == stub::Kind::proj &&
         stub::last_proj.L == 100 && stub::last_proj.D == 256 && stub::last_proj.n_out == 3);
   CHECK(proj(2, 100, 256, 2, 4, 128, false) == ATTN_JVP_OK && stub::last_proj.tx == nullptr);

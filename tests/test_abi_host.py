@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert A.attn_jvp_version() == 10300
+    assert A.attn_jvp_version() == 10400
     assert A.attn_jvp_status_string(0) == "ok"
     assert A.attn_jvp_status_string(A.ATTN_JVP_EUNSUPPORTED).startswith("unsupported")
     assert A.attn_jvp_status_string(99) == "unknown status"
@@ -52,7 +52,7 @@ def call(B=1, H=1, Lq=8, Lk=8, d=64, scale=0.125, dtype=0, ptrs=None, lse=None):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=2), A.ATTN_JVP_EINVAL),
+    (dict(dtype=3), A.ATTN_JVP_EINVAL),
     (dict(dtype=-1), A.ATTN_JVP_EINVAL),
     (dict(B=-1), A.ATTN_JVP_EINVAL),
     (dict(Lk=-3), A.ATTN_JVP_EINVAL),
@@ -201,7 +201,8 @@ def call_proj(ptrs=None, B=1, L=8, D=64, n_out=3, H=2, d=64, dtype=1):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=2), A.ATTN_JVP_EINVAL),
+    (dict(dtype=3), A.ATTN_JVP_EINVAL),
+    (dict(dtype=2), A.ATTN_JVP_EUNSUPPORTED),
     (dict(dtype=0), A.ATTN_JVP_EUNSUPPORTED),
     (dict(L=-1), A.ATTN_JVP_EINVAL),
     (dict(D=-64), A.ATTN_JVP_EINVAL),
@@ -309,7 +310,8 @@ def call_nr(ptrs=None, B=1, H=2, L=8, d=64, eps=1e-6, dtype=1):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=2), A.ATTN_JVP_EINVAL),
+    (dict(dtype=3), A.ATTN_JVP_EINVAL),
+    (dict(dtype=2), A.ATTN_JVP_EUNSUPPORTED),
     (dict(L=-1), A.ATTN_JVP_EINVAL),
     (dict(d=96), A.ATTN_JVP_EUNSUPPORTED),
     (dict(eps=-1e-6), A.ATTN_JVP_EINVAL),
@@ -327,6 +329,7 @@ def call_nr(ptrs=None, B=1, H=2, L=8, d=64, eps=1e-6, dtype=1):
     (dict(L=1 << 31), A.ATTN_JVP_EUNSUPPORTED),
 ])
 def test_rmsnorm_rope_rejects_invalid_arguments(lib, kw, status):
+    """(dtype 2, float32 outputs from bf16 inputs, is for the attention outputs only.)"""
     assert call_nr(**kw) == status
     assert A.attn_jvp_last_error() != ""
 
@@ -341,3 +344,15 @@ def test_rmsnorm_rope_zero_size_and_optional_inputs(lib):
     # no tangent, no gain, no tables: every optional input may be NULL together
     assert call_nr(ptrs=[FAKE, 0, FAKE, 0, 0, 0, 0]) == A.ATTN_JVP_ELAUNCH
     assert call_nr(ptrs=[FAKE] * 7, dtype=0, d=128) == A.ATTN_JVP_ELAUNCH
+
+
+def test_float32_outputs_from_bf16_pass_host_checks(lib):
+    """dtype 2 (bf16 inputs, float32 O and tO; float32 partials merged into a
+    bf16 result) is accepted by fwd, fwd_part and merge."""
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this checks the no-device path only")
+    assert call(dtype=2) == A.ATTN_JVP_ELAUNCH
+    assert A.attn_jvp_fwd_part(*([FAKE] * 10), 1, 1, 8, 8, 8, 64, 0.125, 2) == A.ATTN_JVP_ELAUNCH
+    assert call_merge(dtype=2) == A.ATTN_JVP_ELAUNCH

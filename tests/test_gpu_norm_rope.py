@@ -167,3 +167,37 @@ def test_video_queries_sampled(A):
         return np.unique(np.concatenate([r, np.arange(6), np.arange(w.L - 6, w.L)]))
 
     check(w, y, ty, rows_fn=rows)
+
+
+def test_projection_norm_rope_attention_chain(A):
+    """proj -> rmsnorm_rope (Q and K, in place) -> fwd on the device equals the
+    fp64 composition of the three oracles; the device rounds to bf16 between
+    the layers, which the attention tolerance of the bf16 path covers."""
+    from oracle import attention_jvp_head, projection_jvp
+    from workloads import custom_proj, proj_host_inputs
+    from workloads.device import device_proj_inputs
+
+    pw = custom_proj(1, 230, 256, 3, 2, 128, seed_id=2290)
+    nw = custom_norm_rope(1, 2, 230, 128, seed_id=3500)  # gain and tables for the chain
+    print("case proj -> rmsnorm_rope -> attention", flush=True)
+    h = proj_host_inputs(pw)
+    x = device_proj_inputs(pw)
+    nr = device_norm_rope_inputs(nw)
+    g_k = nr["gamma"].flip(0).contiguous()  # a second gain for the keys
+    y, ty = A.proj(x["x"], x["tx"], x["w"], x["bias"], n_out=3, heads=2)
+    A.rmsnorm_rope(y[0], ty[0], nr["gamma"], nr["cos"], nr["sin"], eps=nw.eps, inplace=True)
+    A.rmsnorm_rope(y[1], ty[1], g_k, nr["cos"], nr["sin"], eps=nw.eps, inplace=True)
+    o, to, lse = A.fwd(y[0], y[1], y[2], ty[0], ty[1], ty[2])
+    torch.cuda.synchronize()
+    Y, TY = projection_jvp(h["x"], h["tx"], h["w"], h["bias"], 3, 2, 128)
+    g = norm_rope_array(nw, "gamma")
+    c, s = rope_tables(nw)
+    Q, TQ = norm_rope_jvp(Y[0, 0], TY[0, 0], g, c, s, nw.eps)
+    K, TK = norm_rope_jvp(Y[1, 0], TY[1, 0], g[::-1], c, s, nw.eps)
+    sc = 128 ** -0.5
+    for hd in range(2):
+        O, tO, L = attention_jvp_head(Q[hd], K[hd], Y[2, 0, hd], TQ[hd], TK[hd], TY[2, 0, hd], sc)
+        eo = np.abs(o[0, hd].float().cpu().numpy() - O).max() / np.abs(O).max()
+        et = np.abs(to[0, hd].float().cpu().numpy() - tO).max() / np.abs(tO).max()
+        print(f"  head {hd}: O {eo:.3e} tO {et:.3e}", flush=True)
+        assert eo <= 2e-2 and et <= 2e-2
