@@ -102,8 +102,9 @@ def distribution_cases(n=24, seed=20261205):
         st = float(rng.choice([0.01, 0.5, 1.0, 10.0]))
         scale = float(10 ** rng.uniform(-2.5, -0.5))
         if dtype == "fp32":
-            # logit std sq^2 * scale * sqrt(d) at most 4: inside what fp32 logits can
-            # carry to the 1e-5 tolerance over these key ranges
+            # logit std sq^2 * scale * sqrt(d) at most 4, half the fp32 envelope's
+            # edge (std 8; tests/test_gpu_fp32_envelope.py covers the edge and
+            # the cases beyond it)
             scale = min(scale, 4.0 / (sq * sq * d ** 0.5))
         n_split = int(rng.choice([1, 1, 2, 5, 16])) if Lk >= 16 else 1
         frozen = bool(rng.random() < 0.25)
