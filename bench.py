@@ -54,6 +54,8 @@ _CSRC = "attention_forward_mode_attn_amd/csrc/"
 KERNEL_SOURCES = {
     "attention": [_CSRC + "kernel_bf16.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
     "proj": [_CSRC + "proj_bf16.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
+    "norm_rope": [_CSRC + "norm_rope.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
+    "merge": [_CSRC + "merge.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
 }
 
 
@@ -392,7 +394,7 @@ def bench_norm_rope(args):
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name, "norm_rope"),
             "kernel": f"norm_rope_kernel<{str(w.dtype == 'bf16').lower()}, {w.d}>",
             "avg_launch_ms": round(avg_launch_ms, 5),
             "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 5),
