@@ -41,14 +41,15 @@ extern "C" {
 
 /* Element type of q, k, v, tq, tk, tv, o and to (lse is always float32). */
 typedef enum {
-  ATTN_JVP_FP32 = 0,        /* float32 in, float32 out, float32 arithmetic.  The
-                               logits scale*q.k are accumulated in float32, so
-                               their error grows with their magnitude: O and tO
+  ATTN_JVP_FP32 = 0,        /* float32 in, float32 out.  The logits q.k are
+                               accumulated in float64 (exact products of the
+                               float32 operands) and each softmax exponent is
+                               formed in float64 and rounded once to float32;
+                               every other product and sum is float32.  O and tO
                                stay within 1e-5 of the largest element of the
-                               exact result while the scaled logits have a
-                               standard deviation up to about 8 (|logit| up to
-                               about 40); at 40 the error is ~2e-5, with logits in
-                               the hundreds ~1e-4 */
+                               exact result whatever the logits' magnitude
+                               (tested up to scaled logits of standard deviation
+                               100, and logits rising into the hundreds) */
   ATTN_JVP_BF16 = 1,        /* bfloat16 in, bfloat16 out (round to nearest even),
                                bf16 matrix products with float32 accumulation */
   ATTN_JVP_BF16_F32OUT = 2  /* bfloat16 inputs as ATTN_JVP_BF16, o and to written as

@@ -89,7 +89,7 @@ def test_projection_random_shape(A, i, B, L, D, n_out, H, d, tangent, bias):
 def distribution_cases(n=24, seed=20261205):
     """Seeded shapes with varied value distributions: operand std (logit std is
     its square at the default scale), tangent std, softmax scale, key shards up
-    to 16, and fp32 over long key ranges, inside the envelope fp32 can meet."""
+    to 16, and fp32 over long key ranges."""
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -101,11 +101,6 @@ def distribution_cases(n=24, seed=20261205):
         sq = float(rng.choice([0.3, 1.0, 2.0] if dtype == "fp32" else [0.3, 1.0, 2.0, 2.83]))
         st = float(rng.choice([0.01, 0.5, 1.0, 10.0]))
         scale = float(10 ** rng.uniform(-2.5, -0.5))
-        if dtype == "fp32":
-            # logit std sq^2 * scale * sqrt(d) at most 4, half the fp32 envelope's
-            # edge (std 8; tests/test_gpu_fp32_envelope.py covers the edge and
-            # the cases beyond it)
-            scale = min(scale, 4.0 / (sq * sq * d ** 0.5))
         n_split = int(rng.choice([1, 1, 2, 5, 16])) if Lk >= 16 else 1
         frozen = bool(rng.random() < 0.25)
         out.append((i, B, H, Lq, Lk, d, dtype, sq, st, scale, n_split, frozen))
