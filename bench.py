@@ -53,6 +53,7 @@ METRIC_PROJ = "projection-JVP TFLOP/s (2*B*L*D*F per product, X and TX) + % bf16
 _CSRC = "attention_forward_mode_attn_amd/csrc/"
 KERNEL_SOURCES = {
     "attention": [_CSRC + "kernel_bf16.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
+    "attention_fp32": [_CSRC + "kernel_fp32.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
     "proj": [_CSRC + "proj_bf16.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
     "norm_rope": [_CSRC + "norm_rope.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
     "merge": [_CSRC + "merge.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
