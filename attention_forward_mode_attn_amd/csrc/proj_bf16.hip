@@ -31,20 +31,18 @@
 //  * the bias initialises the X accumulators; the epilogue rounds to bf16 and
 //    stores 16 bytes per lane after pairing the half-waves with v_permlane32_swap.
 //  * kT = false (a frozen input, no TX): X tiles and accumulators only.
+//  * grids that would leave half the CUs or more idle (at most 128 workgroups
+//    of 256 features) use tiles of 128 features instead, twice as many
+//    workgroups, each wave 32 tokens x 128 features; without a tangent the
+//    hidden step is then 128 wide, so that a step still holds 32 MFMAs per
+//    wave.  Each tile shape has its own step schedule (Sched below).
 #include "device_common.h"
 #include "launch.h"
 
 namespace attnjvp {
 namespace {
 
-constexpr int kTF = 256;                       // output features per workgroup
 constexpr int kTT = kWaves * kWaveRows;        // tokens per workgroup (128)
-constexpr int kTK = 64;                        // hidden-dim elements per step
-constexpr int kRowB = kTK * 2;                 // bytes of one tile row
-constexpr int kWTile = kTF * kRowB;            // 32 KB
-constexpr int kXTile = kTT * kRowB;            // 16 KB
-constexpr int kStageB = kWTile + 2 * kXTile;   // W | X | TX
-constexpr int kFB = kTF / 32;                  // 32-feature blocks per tile
 // Feature tiles per dispatch group: 16 on large grids (each X/TX tile, which does
 // not fit the last-level cache as a whole, is read by 16 workgroups at once);
 // 4 on grids of fewer than 2048 workgroups, where the grid is a few generations
@@ -52,6 +50,38 @@ constexpr int kFB = kTF / 32;                  // 32-feature blocks per tile
 // 9%).
 constexpr int kGroupFLarge = 16, kGroupFSmall = 4, kSmallGrid = 2048;
 constexpr int kRing = 16;                      // W fragment registers in flight
+// Grids of at most this many 256-feature workgroups use 128-feature tiles.
+constexpr int kNarrowGrid = 128;
+
+// Tile geometry: kTF output features x kTT tokens per workgroup, kTK hidden
+// elements per step; rows of kTK bf16 in LDS.
+template <bool kT, int kTF_, int kTK_>
+struct Geom {
+  static constexpr int kTF = kTF_, kTK = kTK_;
+  static constexpr int kFB = kTF / 32;                 // 32-feature blocks (per wave)
+  static constexpr int kC = kTK / 16;                  // 16-wide hidden chunks per step
+  static constexpr int kQ = kFB * kC;                  // W fragments per step
+  static constexpr int kRowB = kTK * 2;                // bytes of one tile row
+  static constexpr int kUPR = kRowB / 16;              // 16-byte units per row
+  static constexpr int kRowsPerSlice = 1024 / kRowB;   // rows of one 1 KB copy slice
+  static constexpr int kWTile = kTF * kRowB;
+  static constexpr int kXTile = kTT * kRowB;
+  static constexpr int kNX = kT ? 2 : 1;               // X fragments per chunk (X, TX)
+  // W | X | TX; the 256-feature tiles keep the TX slot in every stage also
+  // without a tangent (the stage layout their schedules were measured with)
+  static constexpr int kStageB = kWTile + (kTF == 256 ? 2 : kNX) * kXTile;
+  static constexpr int kWDma = kWTile / 1024 / kWaves;   // W slices per wave and step
+  static constexpr int kXDma = kXTile / 1024 / kWaves;   // X (and TX) slices per wave and step
+  static constexpr int kDma = kWDma + kNX * kXDma;
+  static_assert(kRowB == 128 || kRowB == 256, "row swizzle");
+  static_assert(kWTile % (1024 * kWaves) == 0 && kXTile % (1024 * kWaves) == 0, "copy slices");
+  static_assert(kC % 2 == 0, "X chunks alternate between two register slots");
+  // Unit u of tile row r sits at slot u ^ swz(r): the 16 lanes that a
+  // ds_read_b128 serves together read one unit column of 16 consecutive rows,
+  // and the swizzle spreads them over all 16 bank groups of the 64-bank LDS
+  // (128-byte rows: two rows per bank sweep; 256-byte rows: one).
+  static __device__ inline int swz(int r) { return kRowB == 128 ? (r >> 1) & 7 : r & 15; }
+};
 
 struct ProjParams {
   const void* x;
@@ -64,70 +94,92 @@ struct ProjParams {
   int n_ft, n_tt, n_blocks, group_f;
 };
 
-// Unit u (16 bytes) of tile row r sits at slot u ^ swz(r): the 16 lanes that a
-// ds_read_b128 serves together read one unit column of 16 consecutive rows,
-// and the swizzle spreads them over all 16 bank groups of the 64-bank LDS.
-__device__ inline int swz(int r) { return (r >> 1) & 7; }
-
 __device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Per-lane global offset of one 1 KB slice (8 rows x 128 bytes) of a tile whose
+// Per-lane global offset of one 1 KB slice (kRowsPerSlice rows) of a tile whose
 // rows are D elements apart: lane l fills LDS bytes 16l of the slice, i.e. row
-// 8s + l/8, slot l%8, which holds unit (l%8) ^ swz(row) of that row.
+// kRowsPerSlice s + l / kUPR, slot l % kUPR, which holds unit (l % kUPR) ^
+// swz(row) of that row.
+template <class G>
 __device__ inline uint32_t slice_voff(int s, int lane, int D) {
-  const int r = 8 * s + lane / 8;
-  const int u = (lane % 8) ^ swz(r);
+  const int r = G::kRowsPerSlice * s + lane / G::kUPR;
+  const int u = (lane % G::kUPR) ^ G::swz(r);
   return (uint32_t)r * (uint32_t)D * 2u + (uint32_t)u * 16u;
 }
 
-// Schedule of one step (see the file comment).  W fragment q = 8c + fb (hidden
-// chunk c of 16, feature block fb) is used by units q*kPer .. q*kPer + kPer - 1
-// and lives in register slot q % kRing; X fragment c in slot c % 2.  Step k
-// computes on stage k & 1.  Its copies are issued in two parts: kTail slices
-// of step k + 2 right after step k's barrier (from then on no wave reads stage
-// k & 1), and the other slices of step k + 1 in the first units of step k, one
-// every second unit.  The barrier at unit kBar waits for all of them.
-template <bool kT>
-struct Sched {
+// Schedule of one step (see the file comment).  W fragment q = kFB c + fb
+// (hidden chunk c of 16, feature block fb) is used by units q*kPer .. q*kPer +
+// kPer - 1 and lives in register slot q % kRing; X fragment c in slot c % 2.
+// Step k computes on stage k & 1.  Its copies are issued in two parts: kTail
+// slices of step k + 2 right after step k's barrier (from then on no wave reads
+// stage k & 1), and the other slices of step k + 1 in the first units of step
+// k, one every kHeadStride units.  The barrier at unit kBar waits for all of
+// them.  Per tile shape: kLead (W read this many units before its use), kXLead
+// (X read this many units before its chunk starts), kBar, kTail, kHeadStride,
+// and kJoin (how many next-stage reads share the barrier's unit besides X).
+template <bool kT, int kTF, int kTK>
+struct Tune;
+template <>
+struct Tune<true, 256, 64> {
+  static constexpr int kLead = 16, kXLead = 16, kBar = 48, kTail = 12, kHeadStride = 2, kJoin = 0;
+};
+template <>
+struct Tune<false, 256, 64> {
+  static constexpr int kLead = 5, kXLead = 7, kBar = 27, kTail = 4, kHeadStride = 1, kJoin = 0;
+};
+template <>
+struct Tune<true, 128, 64> {
+  static constexpr int kLead = 8, kXLead = 8, kBar = 24, kTail = 6, kHeadStride = 2, kJoin = 0;
+};
+template <>
+struct Tune<false, 128, 128> {
+  static constexpr int kLead = 5, kXLead = 4, kBar = 28, kTail = 4, kHeadStride = 1, kJoin = 1;
+};
+
+template <bool kT, int kTF, int kTK>
+struct Sched : Geom<kT, kTF, kTK>, Tune<kT, kTF, kTK> {
+  using G = Geom<kT, kTF, kTK>;
+  using T = Tune<kT, kTF, kTK>;
   static constexpr int kPer = kT ? 2 : 1;                   // MFMAs per W fragment
-  static constexpr int kUnits = 32 * kPer;                  // MFMAs per step and wave
-  static constexpr int kLead = kT ? 16 : 5;                 // W read this many units before use
-  static constexpr int kPre = (kLead + kPer - 1) / kPer;    // W fragments read in the previous step
-  static constexpr int kXLead = kT ? 16 : 7;                // X read units before chunk c starts
-  static constexpr int kBar = kT ? 48 : 27;                 // unit of the mid-step barrier
-  static constexpr int kNX = kT ? 2 : 1;                    // X fragments per chunk (X, TX)
-  static constexpr int kDma = ((kWTile + kNX * kXTile) / 1024) / kWaves;  // slices per wave
-  static constexpr int kWDma = kWTile / 1024 / kWaves;                    // of which W
-  static constexpr int kTail = kT ? 12 : 4;                 // slices of step k + 2 after the barrier
-  static constexpr int kHeadStride = kT ? 2 : 1;            // units between head copies
-  // unit of the i-th next-stage read (X fragments first, then W 0 .. kPre - 1);
-  // reads that do not fit go to the last unit
-  static constexpr int next_unit(int i) { return kBar + i < kUnits ? kBar + i : kUnits - 1; }
+  static constexpr int kUnits = G::kQ * kPer;               // MFMAs per step and wave
+  static constexpr int kChunkU = G::kFB * kPer;             // units per hidden chunk
+  static constexpr int kPre = (T::kLead + kPer - 1) / kPer; // W fragments read in the previous step
+  // unit of the i-th next-stage read (X fragments first, then W 0 .. kPre - 1;
+  // the first kJoin W reads share the unit of the last X read); reads that do
+  // not fit go to the last unit
+  static constexpr int next_unit(int i) {
+    const int u = T::kBar + (i < G::kNX ? i : (i - T::kJoin < G::kNX - 1 ? G::kNX - 1 : i - T::kJoin));
+    return u < kUnits ? u : kUnits - 1;
+  }
   // a next-stage W fragment goes into a slot whose current fragment is done
   static constexpr bool next_w_slots_free() {
     for (int q2 = 0; q2 < kPre; ++q2)
-      for (int q = q2 % kRing; q < 32; q += kRing)
-        if ((q + 1) * kPer - 1 >= next_unit(kNX + q2)) return false;
+      for (int q = q2 % kRing; q < G::kQ; q += kRing)
+        if ((q + 1) * kPer - 1 >= next_unit(G::kNX + q2)) return false;
     return true;
   }
-  static_assert(31 * kPer - kLead < kBar, "current-stage W reads end before the barrier");
-  static_assert(3 * 8 * kPer - kXLead + kNX - 1 < kBar, "current-stage X reads end before the barrier");
-  static_assert(kLead <= (kRing - 1) * kPer, "a W read does not overwrite a fragment still in use");
-  static_assert(kXLead <= 8 * kPer, "an X read does not overwrite a chunk still in use");
-  static_assert(kBar >= 24 * kPer, "next-stage X chunk 0 (slot 0) is read after chunk 2's last use");
+  static_assert((G::kQ - 1) * kPer - T::kLead < T::kBar, "current-stage W reads end before the barrier");
+  static_assert((G::kC - 1) * kChunkU - T::kXLead + G::kNX - 1 < T::kBar,
+                "current-stage X reads end before the barrier");
+  static_assert(T::kLead <= (kRing - 1) * kPer, "a W read does not overwrite a fragment still in use");
+  static_assert(T::kXLead <= kChunkU, "an X read does not overwrite a chunk still in use");
+  static_assert(next_unit(0) >= (G::kC - 1) * kChunkU,
+                "next-stage X chunk 0 (slot 0) is read after the last use of chunk kC - 2");
   static_assert(next_w_slots_free(), "next-stage W reads do not overwrite fragments still in use");
-  static_assert((kDma - kTail - 1) * kHeadStride < kBar, "head copies issued before the barrier");
-  static_assert(kBar + kTail <= kUnits, "tail copies fit after the barrier");
+  static_assert((G::kDma - T::kTail - 1) * T::kHeadStride < T::kBar, "head copies issued before the barrier");
+  static_assert(T::kBar + T::kTail <= kUnits, "tail copies fit after the barrier");
   // every next-stage fragment is read at least 4 units before its first use
-  static_assert(kUnits - next_unit(kNX + kPre - 1) + (kPre - 1) * kPer >= 4, "next-stage lead");
-  static_assert(kUnits - next_unit(kNX) >= 4, "next-stage lead of W fragment 0");
+  static_assert(kUnits - next_unit(G::kNX + kPre - 1) + (kPre - 1) * kPer >= 4, "next-stage lead");
+  static_assert(kUnits - next_unit(G::kNX) >= 4, "next-stage lead of W fragment 0");
+  static_assert(kUnits - next_unit(G::kNX - 1) >= 4, "next-stage lead of the X fragments");
 };
-template <bool kT>
+template <bool kT, int kTF, int kTK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void proj_bf16_kernel(ProjParams p) {
-  using S = Sched<kT>;
+  using S = Sched<kT, kTF, kTK>;
+  constexpr int kRowB = S::kRowB, kWTile = S::kWTile, kXTile = S::kXTile, kStageB = S::kStageB, kFB = S::kFB;
   __shared__ __attribute__((aligned(1024))) char smem[2 * kStageB];
 
   const int t = threadIdx.x;
@@ -156,12 +208,13 @@ void proj_bf16_kernel(ProjParams p) {
   const auto rx = make_rsrc((const char*)p.x + xoff, (uint32_t)(L - t0) * (uint32_t)D * 2u);
   const auto rtx = make_rsrc(kT ? (const char*)p.tx + xoff : (const char*)p.x, kT ? (uint32_t)(L - t0) * (uint32_t)D * 2u : 0u);
 
-  // This wave's copy slices: W slices 8wv .. 8wv + 7, X (and TX) slices 4wv .. 4wv + 3.
+  // This wave's copy slices: W slices kWDma wv .. kWDma wv + kWDma - 1, X (and
+  // TX) slices kXDma wv .. kXDma wv + kXDma - 1.
   uint32_t voff[S::kDma];
 #pragma unroll
   for (int i = 0; i < S::kDma; ++i) {
-    const int wi = i < S::kWDma ? i : (i - S::kWDma) % 4;
-    voff[i] = slice_voff(i < S::kWDma ? S::kWDma * wv + wi : 4 * wv + wi, lane, D);
+    const int wi = i < S::kWDma ? i : (i - S::kWDma) % S::kXDma;
+    voff[i] = slice_voff<S>(i < S::kWDma ? S::kWDma * wv + wi : S::kXDma * wv + wi, lane, D);
   }
   const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_address(smem));
   // copy slice i of this wave for step k into stage k & 1
@@ -171,19 +224,19 @@ void proj_bf16_kernel(ProjParams p) {
     const uint32_t st = smem_lds + (k & 1) * kStageB;
     if constexpr (i < S::kWDma) {
       lds_dma16(rw, st + (S::kWDma * wv + i) * 1024, voff[i], soff);
-    } else if constexpr (i < S::kWDma + 4) {
-      lds_dma16(rx, st + kWTile + (4 * wv + i - S::kWDma) * 1024, voff[i], soff);
+    } else if constexpr (i < S::kWDma + S::kXDma) {
+      lds_dma16(rx, st + kWTile + (S::kXDma * wv + i - S::kWDma) * 1024, voff[i], soff);
     } else {
-      lds_dma16(rtx, st + kWTile + kXTile + (4 * wv + i - S::kWDma - 4) * 1024, voff[i], soff);
+      lds_dma16(rtx, st + kWTile + kXTile + (S::kXDma * wv + i - S::kWDma - S::kXDma) * 1024, voff[i], soff);
     }
   };
 
   // Fragment offsets in a stage: W fragment (chunk c, block fb) of lane (n, hh)
   // is row 32fb + n, unit 2c + hh; X fragment c is row 32wv + n of the X tile.
-  // Both rows have swz = (n >> 1) & 7.
-  uint32_t lo[4];
+  // Both rows have the swizzle of row n.
+  uint32_t lo[S::kC];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) lo[c] = n * kRowB + (((2 * c + hh) ^ swz(n)) << 4);
+  for (int c = 0; c < S::kC; ++c) lo[c] = n * kRowB + (((2 * c + hh) ^ S::swz(n)) << 4);
   const int xrow = kWTile + wv * 32 * kRowB;
 
   // Accumulators: X products start from the bias (register r of block fb holds
@@ -209,7 +262,7 @@ void proj_bf16_kernel(ProjParams p) {
   bf16x8 wf[kRing], xf[2][2];
   auto read_w = [&](const char* st, auto iq) {
     constexpr int q = decltype(iq)::value;
-    wf[q % kRing] = *reinterpret_cast<const bf16x8*>(st + (q % 8) * 32 * kRowB + lo[q / 8]);
+    wf[q % kRing] = *reinterpret_cast<const bf16x8*>(st + (q % kFB) * 32 * kRowB + lo[q / kFB]);
   };
   auto read_x = [&](const char* st, auto ic, auto iw) {
     constexpr int c = decltype(ic)::value, which = decltype(iw)::value;
@@ -226,20 +279,20 @@ void proj_bf16_kernel(ProjParams p) {
     const char* nxt = smem + ((k + 1) & 1) * kStageB;
     static_for<0, S::kUnits>([&](auto iu) {
       constexpr int u = decltype(iu)::value;
-      constexpr int q = u / S::kPer, c = q / 8, fb = q % 8, which = u % S::kPer;
+      constexpr int q = u / S::kPer, c = q / kFB, fb = q % kFB, which = u % S::kPer;
       acc[which][fb] = mfma(wf[q % kRing], xf[c & 1][which], acc[which][fb]);
       if constexpr (kMore && u % S::kHeadStride == 0 && u / S::kHeadStride < S::kDma - S::kTail)
         issue(k + 1, IC<S::kTail + u / S::kHeadStride>{});
       // current stage: W fragment q2 read kLead units before its first use
-      static_for<S::kPre, 32>([&](auto iq) {
+      static_for<S::kPre, S::kQ>([&](auto iq) {
         constexpr int q2 = decltype(iq)::value;
         if constexpr (q2 * S::kPer - S::kLead == u) read_w(cur, iq);
       });
-      static_for<1, 4>([&](auto ic) {
+      static_for<1, S::kC>([&](auto ic) {
         constexpr int c2 = decltype(ic)::value;
         static_for<0, S::kNX>([&](auto iw) {
           constexpr int w2 = decltype(iw)::value;
-          if constexpr (c2 * 8 * S::kPer - S::kXLead + w2 == u) read_x(cur, ic, iw);
+          if constexpr (c2 * S::kChunkU - S::kXLead + w2 == u) read_x(cur, ic, iw);
         });
       });
       if constexpr (kMore) {
@@ -261,7 +314,7 @@ void proj_bf16_kernel(ProjParams p) {
     });
   };
 
-  const int nk = D / kTK;
+  const int nk = D / kTK;  // the host checks that kTK divides D
   // prologue: step 0's tiles, then its first fragments
   static_for<0, S::kDma>([&](auto ii) { issue(0, ii); });
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -316,7 +369,7 @@ void proj_bf16_kernel(ProjParams p) {
   }
 }
 
-template <bool kT>
+template <bool kT, int kTF, int kTK>
 hipError_t launch(const ProjProblem& pr, hipStream_t stream) {
   ProjParams p;
   p.x = pr.x; p.tx = pr.tx; p.w = pr.w; p.bias = pr.bias; p.y = pr.y; p.ty = pr.ty;
@@ -326,13 +379,25 @@ hipError_t launch(const ProjProblem& pr, hipStream_t stream) {
   p.n_tt = (p.L + kTT - 1) / kTT;
   p.n_blocks = p.n_ft * p.n_tt * p.B;
   p.group_f = p.n_blocks < kSmallGrid ? kGroupFSmall : kGroupFLarge;
-  return launch_1d(reinterpret_cast<const void*>(&proj_bf16_kernel<kT>), p.n_blocks, kThreads, p, stream);
+  return launch_1d(reinterpret_cast<const void*>(&proj_bf16_kernel<kT, kTF, kTK>), p.n_blocks, kThreads, p,
+                   stream);
+}
+
+// Workgroups of the 256-feature tiling (each factor bounded by the host checks).
+int64_t wide_grid(const ProjProblem& p) {
+  const int64_t F = (int64_t)p.n_out * p.H * p.d;
+  return ((F + 255) / 256) * (((int64_t)p.L + kTT - 1) / kTT) * p.B;
 }
 
 }  // namespace
 
 hipError_t launch_proj(const ProjProblem& p, hipStream_t stream) {
-  return p.tx ? launch<true>(p, stream) : launch<false>(p, stream);
+  // At most kNarrowGrid wide workgroups would leave half the CUs or more idle:
+  // 128-feature tiles double the workgroups (the frozen tiles' 128-wide hidden
+  // step needs D % 128 == 0; otherwise the wide tiles run).
+  const bool narrow = wide_grid(p) <= kNarrowGrid;
+  if (p.tx) return narrow ? launch<true, 128, 64>(p, stream) : launch<true, 256, 64>(p, stream);
+  return narrow && p.D % 128 == 0 ? launch<false, 128, 128>(p, stream) : launch<false, 256, 64>(p, stream);
 }
 
 }  // namespace attnjvp

@@ -60,6 +60,16 @@ KERNEL_SOURCES = {
 }
 
 
+def proj_kernel_name(w) -> str:
+    """The projection kernel instantiation a launch of workload ``w`` runs: grids
+    of at most 128 workgroups of 256 features use 128-feature tiles (without a
+    tangent with a 128-wide hidden step, when D % 128 == 0)."""
+    wide = -(-w.n_out * w.H * w.d // 256) * -(-w.L // 128) * w.B
+    if wide <= 128 and (w.tangent or w.D % 128 == 0):
+        return f"proj_bf16_kernel<{str(w.tangent).lower()}, 128, {64 if w.tangent else 128}>"
+    return f"proj_bf16_kernel<{str(w.tangent).lower()}, 256, 64>"
+
+
 def kernel_source_hash(kernel: str = "attention") -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kernel]:
@@ -509,7 +519,7 @@ def bench_proj(args):
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic(w.name, "proj"),
-            "kernel": f"proj_bf16_kernel<{str(w.tangent).lower()}>",
+            "kernel": proj_kernel_name(w),
             "avg_launch_ms": round(avg_launch_ms, 4),
             "median_launch_ms": round(launch_ms[len(launch_ms) // 2], 4),
             "min_launch_ms": round(launch_ms[0], 4),

@@ -69,6 +69,61 @@ SHAPES = [
 ]
 
 
+# Grids of at most 128 workgroups of the 256-feature tiling run 128-feature
+# tiles (without a tangent with a 128-wide hidden step when D % 128 == 0).
+def wide_grid(B, L, n_out, H, d):
+    return -(-n_out * H * d // 256) * -(-L // 128) * B
+
+
+TILE_SHAPES = [
+    # (B, L, D, n_out, H, d, tangent, bias): narrow tiles
+    (1, 100, 128, 3, 1, 64, False, True),     # frozen, one 128-wide step, partial feature tile (192)
+    (2, 257, 256, 2, 2, 64, False, True),     # frozen, two steps, ragged tokens
+    (1, 130, 384, 3, 2, 128, False, False),   # frozen, three steps, no bias
+    (1, 90, 64, 3, 1, 64, True, True),        # tangent, one 64-wide step, partial feature tile
+    (2, 200, 192, 1, 3, 128, True, False),    # tangent, three steps
+    (1, 5376, 128, 3, 2, 128, False, True),   # frozen at the switch: 42 token x 3 feature tiles = 126
+    (1, 5376, 64, 3, 2, 128, True, True),     # tangent at the switch
+    # wide tiles
+    (1, 5504, 128, 3, 2, 128, False, True),   # frozen just past the switch: 129 workgroups
+    (1, 5504, 64, 3, 2, 128, True, True),     # tangent just past the switch
+    (1, 4096, 256, 2, 8, 128, False, True),   # frozen, 256 workgroups
+    (1, 200, 192, 2, 2, 64, False, True),     # frozen narrow grid, D % 128 != 0: wide tiles
+]
+
+
+@pytest.mark.parametrize("B,L,D,n_out,H,d,tangent,bias", TILE_SHAPES)
+def test_tile_shapes_match_oracle(A, B, L, D, n_out, H, d, tangent, bias):
+    narrow = wide_grid(B, L, n_out, H, d) <= 128 and (tangent or D % 128 == 0)
+    w = custom_proj(B, L, D, n_out, H, d, tangent=tangent, bias=bias, seed_id=2300 + L + D + n_out)
+    print(f"case proj {'narrow' if narrow else 'wide'} tiles B{B} L{L} D{D} n_out{n_out} H{H} d{d} "
+          f"tangent={tangent} bias={bias}", flush=True)
+    run_case(A, w)
+
+
+@pytest.mark.parametrize("tangent", [False, True])
+def test_narrow_tiles_equal_wide_tiles_bitwise(A, tangent):
+    """Both tilings sum each output's hidden chunks of 16 in the same order, so a
+    batch element projected alone (a narrow grid) and inside a batch large enough
+    for the wide tiles must agree bit for bit."""
+    L, D, n_out, H, d = 300, 256, 3, 2, 64
+    B = 1
+    while wide_grid(B, L, n_out, H, d) <= 128:
+        B += 1
+    assert wide_grid(1, L, n_out, H, d) <= 128
+    w = custom_proj(B, L, D, n_out, H, d, tangent=tangent, seed_id=2400 + int(tangent))
+    print(f"case proj narrow vs wide bitwise B{B} L{L} D{D} tangent={tangent}", flush=True)
+    x = device_proj_inputs(w)
+    y, ty = A.proj(x["x"], x["tx"], x["w"], x["bias"], n_out=n_out, heads=H)
+    x1 = x["x"][:1].contiguous()
+    tx1 = x["tx"][:1].contiguous() if tangent else None
+    y1, ty1 = A.proj(x1, tx1, x["w"], x["bias"], n_out=n_out, heads=H)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:, :1], y1)
+    if tangent:
+        assert torch.equal(ty[:, :1], ty1)
+
+
 @pytest.mark.parametrize("B,L,D,n_out,H,d,tangent,bias", SHAPES)
 def test_projection_matches_oracle(A, B, L, D, n_out, H, d, tangent, bias):
     w = custom_proj(B, L, D, n_out, H, d, tangent=tangent, bias=bias, seed_id=2100 + L + D)
