@@ -123,3 +123,56 @@ def test_projection_then_attention_replays_in_a_graph(A):
         torch.cuda.synchronize()
         for got, want in zip(ys + att, ref):
             assert torch.equal(got, want), i
+
+
+def test_layer_chain_with_norm_and_rotary_replays_in_a_graph(A):
+    """Projection with its tangent, then the RMS normalisation and rotary
+    embedding of Q and K in place, then the attention JVP: the whole chain in
+    one captured graph, every replay bit for bit the eager result."""
+    from workloads import custom_proj
+    from workloads.device import device_proj_inputs
+
+    B, L, D, H, d = 1, 150, 256, 2, 64
+    w = custom_proj(B, L, D, 3, H, d, seed_id=7300)
+    print("case graph projection + norm/rotary + attention", flush=True)
+    x = device_proj_inputs(w)
+    g_q = (1.0 + 0.1 * torch.randn(d, generator=torch.Generator().manual_seed(7301))).to(torch.bfloat16).cuda()
+    g_k = (1.0 + 0.1 * torch.randn(d, generator=torch.Generator().manual_seed(7302))).to(torch.bfloat16).cuda()
+    pos = torch.arange(L, dtype=torch.float64)[:, None]
+    ang = pos * 10000.0 ** (-torch.arange(0, d, 2, dtype=torch.float64) / d)
+    cos, sin = ang.cos().float().contiguous().cuda(), ang.sin().float().contiguous().cuda()
+
+    def chain(ys, att):
+        A.proj(x["x"], x["tx"], x["w"], x["bias"], n_out=3, heads=H, out=ys)
+        A.rmsnorm_rope(ys[0][0], ys[1][0], g_q, cos, sin, inplace=True)
+        A.rmsnorm_rope(ys[0][1], ys[1][1], g_k, cos, sin, inplace=True)
+        A.fwd(ys[0][0], ys[0][1], ys[0][2], ys[1][0], ys[1][1], ys[1][2], out=att)
+
+    shape = (3, B, H, L, d)
+    ref_ys = (torch.empty(shape, dtype=torch.bfloat16, device="cuda"), torch.empty(shape, dtype=torch.bfloat16, device="cuda"))
+    ref_att = (torch.empty((B, H, L, d), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((B, H, L, d), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((B, H, L), dtype=torch.float32, device="cuda"))
+    chain(ref_ys, ref_att)
+    torch.cuda.synchronize()
+    ref = list(ref_ys) + list(ref_att)
+    ys = tuple(torch.empty_like(t) for t in ref_ys)
+    att = tuple(torch.empty_like(t) for t in ref_att)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        chain(ys, att)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        chain(ys, att)
+    for i in range(4):
+        for t in ys + att:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(ys + att, ref):
+            assert torch.equal(got, want), i
