@@ -40,6 +40,7 @@ namespace {
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBcF = 32;  // keys per tile
+constexpr double kLog2eD = 1.4426950408889634;  // log2(e), for the fp64 exponents
 
 struct Params {
   const void* q;
@@ -167,7 +168,7 @@ void attn_jvp_fp32_kernel(Params p) {
   float st_m[2] = {-INFINITY, -INFINITY}, st_l[2] = {0.0f, 0.0f}, st_a[2] = {0.0f, 0.0f};
   const float scale = p.scale;
   const float c2f = scale * kLog2e;
-  const double c2d = (double)scale * 1.4426950408889634;
+  const double c2d = (double)scale * kLog2eD;
 
   // P and P*tS of one tile: pv[kb][qb][i] is the weight of key 16 kb + g + 4 i
   // for query 16 qb + n.  Two-level sums: the tile's contributions to l, a and
