@@ -33,7 +33,12 @@
 //    one unit apart so that no unit waits on its own results;
 //  * variants: a frozen context (tK = tV = 0) skips the tK and tV products
 //    and copies; a key shard (kv_rows > Lk) is the same pass on part of the
-//    keys, with the tangent of lse as an extra output for an exact merge.
+//    keys, with the tangent of lse as an extra output for an exact merge;
+//  * d = 64: a tile holds half the MFMAs for the same softmax work, and the
+//    registers allow two waves per SIMD (two workgroups per CU, 64 KB of LDS
+//    each): the tiles then run one at a time (logits, softmax, products, no
+//    logits carried across tiles), and the other wave's MFMAs hide each
+//    wave's softmax.
 #include "device_common.h"
 #include "launch.h"
 
@@ -130,7 +135,7 @@ __device__ inline void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
 // kFrozen: the key-side tangents are zero (tK = tV = 0, a frozen context):
 // the tK Q^T and tV P^T products and the tK/tV tile copies are skipped.
 template <int D, bool kFrozen>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1)))
 void attn_jvp_bf16_kernel(Params p) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::kStage];
@@ -431,6 +436,47 @@ void attn_jvp_bf16_kernel(Params p) {
   const bool ragged = (Lk % kBc) != 0;
   float my;  // row max of y over the tile waiting in (yv, tsv)
 
+  if constexpr (D == 64) {
+    // Two waves per SIMD: one tile at a time, no logits carried across tiles
+    // (195 registers).  Tile j + 1 is copied into the other stage, released by
+    // the barrier that opens tile j, while tile j is used.
+    issue(0, 0);
+    issue(0, 2);
+    for (int j = 0; j < nt; ++j) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile j landed
+      __syncthreads();                     // ... for every wave; tile j - 1 is no longer read
+      if (j + 1 < nt) {
+        issue(j + 1, 0);
+        issue(j + 1, 2);
+      }
+      const char* stage = smem + (j & 1) * C::kStage;
+      f32x16 sn[2], tsn[2];
+      static_for<0, C::kChunksD>([&](auto ic) {
+        bf16x8 k[4];
+        load_k(stage, decltype(ic)::value, k);
+        static_for<0, kUPC>([&](auto iu) { logit_mfma(iu, ic, k, sn, tsn); });
+      });
+      if (j == nt - 1 && ragged) mask_tail<2>(sn, Lk - j * kBc, hh);
+      const float mt = tile_max_log2<2>(sn, c2);
+      if (needs_rescale(st, mt)) {
+        const float alpha = apply_rescale(st, mt);
+#pragma unroll
+        for (int b = 0; b < C::kBlocksD; ++b) {
+          acc_o[b] *= alpha;
+          acc_t[b] *= alpha;
+        }
+      }
+      Take tk;
+      tk.mx = -INFINITY;
+      all_steps(IC<0>{}, IC<64>{}, IC<2>{}, [&](auto is, auto ix) { take_step(is, ix, tk, sn, tsn); });
+      Probs pr;
+      all_steps(IC<0>{}, IC<32>{}, IC<4>{}, [&](auto is, auto ie) { elem_step(is, ie, pr); });
+      sum_a(pr);
+      bf16x8 vf[C::kBlocksD], tvf[C::kBlocksD];
+      load_v0(stage, vf, tvf);
+      products(stage, pr, vf, tvf, [](auto) {});
+    }
+  } else {
   // ---- prologue: tile 0 logits; its max sets the exponent base --------------
   // The tile-0 logits need Q and K|tK of tile 0 only: the later copies (V|tV
   // of tile 0, K|tK of tile 1) keep landing under them.  Vector memory
@@ -574,6 +620,7 @@ void attn_jvp_bf16_kernel(Params p) {
     products(smem + (j & 1) * C::kStage, pr, vf, tvf, [](auto) {});
   }
 
+  }  // D != 64
   // ---- epilogue ------------------------------------------------------------
   const float l = xhalf_sum(st.l), a = xhalf_sum(st.a);
   const float inv = 1.0f / l, mu = a * inv;
