@@ -100,3 +100,20 @@ def test_norm_rope_workload_is_checked():
     r = bench("--norm-rope", "nope")
     assert r.returncode == 2
     assert "q_video_bf16" in r.stderr
+
+
+def test_projection_kernel_name_follows_the_tile_switch():
+    """The bench line names the projection instantiation a launch runs: 128-feature
+    tiles when the 256-feature grid has at most 128 workgroups (without a
+    tangent only when D % 128 == 0), else 256-feature tiles."""
+    import bench
+    from workloads import PROJ_WORKLOADS, custom_proj
+
+    assert bench.proj_kernel_name(PROJ_WORKLOADS["qkv_video_bf16"]) == "proj_bf16_kernel<true, 256, 64>"
+    assert bench.proj_kernel_name(PROJ_WORKLOADS["qkv_image_bf16"]) == "proj_bf16_kernel<true, 256, 64>"
+    assert bench.proj_kernel_name(PROJ_WORKLOADS["kv_text_frozen_bf16"]) == "proj_bf16_kernel<false, 128, 128>"
+    # 42 token tiles x 3 feature tiles = 126 workgroups: narrow; 43 x 3 = 129: wide
+    assert bench.proj_kernel_name(custom_proj(1, 5376, 64, 3, 2, 128)) == "proj_bf16_kernel<true, 128, 64>"
+    assert bench.proj_kernel_name(custom_proj(1, 5504, 64, 3, 2, 128)) == "proj_bf16_kernel<true, 256, 64>"
+    assert bench.proj_kernel_name(custom_proj(1, 200, 192, 2, 2, 64, tangent=False)) == \
+        "proj_bf16_kernel<false, 256, 64>"
