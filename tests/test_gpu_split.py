@@ -186,3 +186,21 @@ def test_float32_partials_on_text_cross_config(A):
                                    f32_partials=True)
     torch.cuda.synchronize()
     check(w, compare(w, o, to, lse, rows_fn=lambda b, h: sample_rows(w, b, h), tlse=tlse), "text cross f32 parts")
+
+
+def test_split_on_video_self_config(A):
+    """The key-shard path at full size in the configuration `bench.py --split 4`
+    times (4 shards of the 32760 keys, then the merge), with bf16 and with
+    float32 partials, on sampled rows of every head (both edges of the first
+    query tile, rows of the ragged tail tile, seeded random rows)."""
+    w = WORKLOADS["video_self_bf16"]
+    x = device_inputs(w)
+    for f32_partials in (False, True):
+        kind = "f32" if f32_partials else "bf16"
+        print(f"case {w.name} 4 shards, {kind} partials (sampled rows)", flush=True)
+        o, to, lse, tlse = A.fwd_split(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], 4, scale=w.scale,
+                                       f32_partials=f32_partials)
+        torch.cuda.synchronize()
+        check(w, compare(w, o, to, lse, rows_fn=lambda b, h: sample_rows(w, b, h, n_random=24), tlse=tlse),
+              f"video self {kind} parts")
+        del o, to, lse, tlse
