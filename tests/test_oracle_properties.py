@@ -138,3 +138,79 @@ def test_complex_step_pin_rejects_planted_mistakes():
     assert all(_complex_step_holds(_variant(None), pr) for pr in cases)
     for mistake in ("unscaled tS", "tK dropped", "mu dropped", "V for tV", "lse in base 2"):
         assert not all(_complex_step_holds(_variant(mistake), pr) for pr in cases), mistake
+
+
+# ---- the layers in front of attention ------------------------------------------
+
+
+@st.composite
+def projections(draw):
+    B, L, D = draw(st.integers(1, 2)), draw(st.integers(1, 4)), draw(st.integers(1, 6))
+    n_out, H, d = draw(st.integers(1, 3)), draw(st.integers(1, 2)), draw(st.integers(1, 3))
+    seed = draw(st.integers(0, 2**31 - 1))
+    rng = np.random.default_rng(seed)
+    x, tx = (rng.standard_normal((B, L, D)) for _ in range(2))
+    w = rng.standard_normal((n_out * H * d, D))
+    bias = rng.standard_normal(n_out * H * d) if draw(st.booleans()) else None
+    return x, tx, w, bias, n_out, H, d
+
+
+@given(projections())
+@settings(**SETTINGS)
+def test_projection_tangent_is_the_complex_step_derivative(pr):
+    """Y = x W^T + b written out per output element in complex arithmetic, then
+    laid out [n, b, h, t, j] with feature f = (n H + h) d + j."""
+    from oracle import projection_jvp
+
+    x, tx, w, bias, n_out, H, d = pr
+    hstep = 1e-30
+    xc = x + 1j * hstep * tx
+    B, L, D = x.shape
+    Yc = np.zeros((n_out, B, H, L, d), dtype=complex)
+    for n in range(n_out):
+        for h in range(H):
+            for j in range(d):
+                f = (n * H + h) * d + j
+                Yc[n, :, h, :, j] = (xc * w[f]).sum(axis=-1) + (0.0 if bias is None else bias[f])
+    Y, TY = projection_jvp(x, tx, w, bias, n_out, H, d)
+    assert np.allclose(Y, Yc.real, rtol=1e-12, atol=1e-12)
+    assert np.allclose(TY, Yc.imag / hstep, rtol=1e-12, atol=1e-12)
+
+
+@st.composite
+def norm_rope_cases(draw):
+    L, half = draw(st.integers(1, 4)), draw(st.integers(1, 4))
+    seed = draw(st.integers(0, 2**31 - 1))
+    rng = np.random.default_rng(seed)
+    x, tx = (draw(st.sampled_from([0.1, 1.0, 5.0])) * rng.standard_normal((2, L, 2 * half)) for _ in range(2))
+    gamma = 1.0 + 0.3 * rng.standard_normal(2 * half) if draw(st.booleans()) else None
+    if draw(st.booleans()):
+        ang = rng.uniform(-np.pi, np.pi, size=(L, half))
+        cos, sin = np.cos(ang), np.sin(ang)
+    else:
+        cos = sin = None
+    eps = draw(st.sampled_from([0.0, 1e-6, 0.5]))
+    return x, tx, gamma, cos, sin, eps
+
+
+@given(norm_rope_cases())
+@settings(**SETTINGS)
+def test_norm_rope_tangent_is_the_complex_step_derivative(pr):
+    """The RMS normalisation (x^2, not |x|^2, so the map is analytic) and the
+    rotation of each pair (2i, 2i+1), written in complex arithmetic."""
+    from oracle import norm_rope_jvp
+
+    x, tx, gamma, cos, sin, eps = pr
+    hstep = 1e-30
+    xc = x + 1j * hstep * tx
+    n = xc / np.sqrt(np.mean(xc * xc, axis=-1, keepdims=True) + eps)
+    if gamma is not None:
+        n = n * gamma
+    if cos is not None:
+        even, odd = n[..., 0::2].copy(), n[..., 1::2].copy()
+        n = n.copy()
+        n[..., 0::2] = cos * even - sin * odd
+        n[..., 1::2] = sin * even + cos * odd
+    y, ty = norm_rope_jvp(x, tx, gamma, cos, sin, eps)
+    assert np.allclose(y, n.real, rtol=1e-12, atol=1e-12)
+    assert np.allclose(ty, n.imag / hstep, rtol=1e-9, atol=1e-9 * max(1.0, np.abs(ty).max()))
