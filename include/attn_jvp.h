@@ -49,9 +49,20 @@ typedef enum {
                                stay within 1e-5 of the largest element of the
                                exact result whatever the logits' magnitude
                                (tested up to scaled logits of standard deviation
-                               100, and logits rising into the hundreds) */
+                               100, and logits rising into the hundreds).
+                               Key shards merged by attn_jvp_merge carry each
+                               shard's float32 lse: their weights are exact to
+                               about 2^-24 |lse|, so at |lse| near 1000 the
+                               merged O and tO are off by up to ~2.5e-5 */
   ATTN_JVP_BF16 = 1,        /* bfloat16 in, bfloat16 out (round to nearest even),
-                               bf16 matrix products with float32 accumulation */
+                               bf16 matrix products with float32 accumulation.
+                               P and P*tS meet V as bf16 values while l sums the
+                               float32 P, so on softmax rows whose weight sits
+                               on a few keys with tangent logits of tens, tO is
+                               off by about 2^-9 |scale*tS| |V| (measured up to
+                               4.3e-2 of tO's largest element at scaled-logit
+                               standard deviations 65-130); ordinary rows stay
+                               within 2e-2 */
   ATTN_JVP_BF16_F32OUT = 2  /* bfloat16 inputs as ATTN_JVP_BF16, o and to written as
                                float32 (attn_jvp_fwd, attn_jvp_fwd_part); for
                                attn_jvp_merge: float32 partials, bfloat16 result.
