@@ -204,3 +204,20 @@ def test_split_on_video_self_config(A):
         check(w, compare(w, o, to, lse, rows_fn=lambda b, h: sample_rows(w, b, h, n_random=24), tlse=tlse),
               f"video self {kind} parts")
         del o, to, lse, tlse
+
+
+def test_cp_shard_config_unsplit_and_split(A):
+    """One GPU's share of the video layer under head and query sharding (5
+    heads, 4095 queries, 32760 keys; 160 workgroups): the single pass and the
+    4-shard path on sampled rows of every head."""
+    w = WORKLOADS["video_self_cp_shard_bf16"]
+    x = device_inputs(w)
+    print(f"case {w.name} single pass over all keys (sampled rows)", flush=True)
+    o, to, lse, tlse = A.fwd_part(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], 0, w.Lk, scale=w.scale)
+    torch.cuda.synchronize()
+    check(w, compare(w, o, to, lse, rows_fn=lambda b, h: sample_rows(w, b, h, n_random=48), tlse=tlse), "cp shard")
+    print(f"case {w.name} 4 shards (sampled rows)", flush=True)
+    o, to, lse, tlse = A.fwd_split(x["q"], x["k"], x["v"], x["tq"], x["tk"], x["tv"], 4, scale=w.scale)
+    torch.cuda.synchronize()
+    check(w, compare(w, o, to, lse, rows_fn=lambda b, h: sample_rows(w, b, h, n_random=48), tlse=tlse),
+          "cp shard 4 parts")

@@ -99,6 +99,11 @@ WORKLOADS = {
             description="the video self-attention layer's width split into 80 heads of 64",
         ),
         Workload(
+            "video_self_cp_shard_bf16", 8, B=1, H=5, Lq=4095, Lk=32760, d=128, dtype="bf16", std=_std(),
+            description="one GPU's share of the video self-attention layer sharded 8 ways over heads and 8 "
+            "over queries (5 heads, 4095 queries, all 32760 keys): 160 workgroups, fewer than the CUs",
+        ),
+        Workload(
             "video_cross_stress_bf16", 5, B=1, H=40, Lq=32760, Lk=512, d=128, dtype="bf16",
             std=_std(q=_SQRT8, k=_SQRT8), per_head_tq_scale=True,
             description="video cross-attention with peaky softmax (logit std ~ 8) and "
