@@ -2,7 +2,7 @@
 queries or keys, with their forward-mode derivative.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
-execute this module: only the test suite, the smoke check of the graft entry
+execute this module: only the test suite, the smoke check of the entry
 point and the ``cpu_baseline`` leg of the benchmark use it.  It shares no code,
 constant or helper with the HIP library; the two meet only through the seeded
 inputs of ``workloads/``.
