@@ -144,11 +144,13 @@ __device__ inline u32x4 pair_halves(u32x2 x, u32x2 y) {
 __device__ inline int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
 // Running per-query state.  m: max (log2 domain) used for exponentiation;
-// l, a: this lane's partial sums of p and p*tS over its half of the keys.
+// l, a: this lane's partial sums of p and p*tS over its half of the keys;
+// lb: of bf16(p), the weights the products consume (bf16 kernel only).
 struct RowState {
   float m;
   float l;
   float a;
+  float lb;
 };
 
 // Mask keys >= valid (tile-relative) of a tile made of NB 32-key blocks.
@@ -178,7 +180,7 @@ __device__ inline bool needs_rescale(const RowState& st, float mt) {
 }
 
 // Move the exponent base of the rows that need it; returns each row's factor
-// (1 for the others) and rescales st.l and st.a.  The caller rescales its matrix
+// (1 for the others) and rescales st.l, st.a and st.lb.  The caller rescales its matrix
 // accumulators by the returned factor.
 __device__ inline float apply_rescale(RowState& st, float mt) {
   const bool need = mt > st.m + kRescaleSlack;
@@ -187,6 +189,7 @@ __device__ inline float apply_rescale(RowState& st, float mt) {
   st.m = m_new;
   st.l *= alpha;
   st.a *= alpha;
+  st.lb *= alpha;
   return alpha;
 }
 

@@ -178,7 +178,7 @@ void attn_jvp_bf16_kernel(Params p) {
     acc_o[b] = f32x16{};
     acc_t[b] = f32x16{};
   }
-  RowState st = {-INFINITY, 0.0f, 0.0f};
+  RowState st = {-INFINITY, 0.0f, 0.0f, 0.0f};
   const float scale = p.scale;
   const float c2 = scale * kLog2e;
 
@@ -306,9 +306,10 @@ void attn_jvp_bf16_kernel(Params p) {
   };
   // Softmax element e: p = 2^y, q = p * ts.  P and P*tS become bf16 B
   // operands, packed in pairs: chunk cc (keys 16cc..16cc+15) is elements
-  // 8cc .. 8cc + 7.  l += p is summed in fp32 (it sets O's normaliser and the
-  // log-sum-exp); a += q is taken over the packed bf16 pairs (sum_a), the same
-  // rounded values that the tO products consume.
+  // 8cc .. 8cc + 7.  l += p is summed in fp32 (it sets the log-sum-exp); lb
+  // and a are taken over the packed bf16 pairs (sum_a), the same rounded
+  // weights and products that the O and tO products consume, so that O and tO
+  // are normalised by the weights they were built from.
   // Four steps per element: exp; q and l; pack (odd e); the operands.
   struct Probs {
     bf16x8 pf[4], ptf[4];
@@ -340,19 +341,22 @@ void attn_jvp_bf16_kernel(Params p) {
       pr.ptf[cc][i + 1] = __builtin_bit_cast(bf16x2, pr.qq[e >> 1])[1];
     }
   };
-  // a += the 32 rounded products of the tile: one v_dot2 with (1, 1) per
-  // packed pair, all 16 in one unit as four independent chains.  On gfx950 the
-  // first v_dot2 after an MFMA waits ~17 cycles and each further one issues in
-  // 4, so one batch per tile costs ~80 cycles where a v_dot2 in every other
-  // unit cost ~270.
+  // a += the 32 rounded products and lb += the 32 rounded weights of the
+  // tile: one v_dot2 with (1, 1) per packed pair, all 32 in one unit as
+  // independent chains.  On gfx950 the first v_dot2 after an MFMA waits ~17
+  // cycles and each further one issues in 4, so one batch per tile costs
+  // little where a v_dot2 in every other unit cost ~270 cycles per tile.
   auto sum_a = [&](const Probs& pr) {
-    float s4[4];
+    float s4[4], b4[4];
     static_for<0, 16>([&](auto ix) {
       constexpr int x = decltype(ix)::value;
       s4[x & 3] = sum_bf16x2(pr.qq[x], x == 0 ? st.a : (x < 4 ? 0.0f : s4[x & 3]));
+      b4[x & 3] = sum_bf16x2(pr.pp[x], x == 0 ? st.lb : (x < 4 ? 0.0f : b4[x & 3]));
     });
     st.a = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    st.lb = (b4[0] + b4[1]) + (b4[2] + b4[3]);
     pin(st.a);
+    pin(st.lb);
   };
   // Software pipeline over a sequence of N units that handle n items (N
   // units, items [g n / N, (g + 1) n / N) start in unit g): unit g runs step s
@@ -577,6 +581,7 @@ void attn_jvp_bf16_kernel(Params p) {
     st.m += delta;
     st.l *= alpha;
     st.a *= alpha;
+    st.lb *= alpha;
 #pragma unroll
     for (int x = 0; x < 32; ++x) yv[x] -= delta;
 #pragma unroll
@@ -622,8 +627,11 @@ void attn_jvp_bf16_kernel(Params p) {
 
   }  // D != 64
   // ---- epilogue ------------------------------------------------------------
-  const float l = xhalf_sum(st.l), a = xhalf_sum(st.a);
-  const float inv = 1.0f / l, mu = a * inv;
+  // O and tO are normalised by the sum of the bf16 weights they were built
+  // from (so the centring cancels exactly where one key carries the row), the
+  // log-sum-exp by the fp32 sum.
+  const float l = xhalf_sum(st.l), lb = xhalf_sum(st.lb), a = xhalf_sum(st.a);
+  const float inv = 1.0f / lb, mu = a * inv;
   if (p.out_f32) {
     // float32 O and tO (the partial results of a key shard, rounded to bf16
     // only once, after the merge): group g of a lane is 4 consecutive dims,

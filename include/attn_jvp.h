@@ -56,13 +56,13 @@ typedef enum {
                                merged O and tO are off by up to ~2.5e-5 */
   ATTN_JVP_BF16 = 1,        /* bfloat16 in, bfloat16 out (round to nearest even),
                                bf16 matrix products with float32 accumulation.
-                               P and P*tS meet V as bf16 values while l sums the
-                               float32 P, so on softmax rows whose weight sits
-                               on a few keys with tangent logits of tens, tO is
-                               off by about 2^-9 |scale*tS| |V| (measured up to
-                               4.3e-2 of tO's largest element at scaled-logit
-                               standard deviations 65-130); ordinary rows stay
-                               within 2e-2 */
+                               P and P*tS meet V as bf16 values; O and tO are
+                               normalised by the sum of those bf16 weights (lse
+                               by the float32 sum), so the tangent-logit
+                               centring cancels where one key carries a row.
+                               Tested within 2e-2 of tO's and O's largest
+                               element up to scaled-logit standard deviations
+                               of 65-130 with tangent logits of tens */
   ATTN_JVP_BF16_F32OUT = 2  /* bfloat16 inputs as ATTN_JVP_BF16, o and to written as
                                float32 (attn_jvp_fwd, attn_jvp_fwd_part); for
                                attn_jvp_merge: float32 partials, bfloat16 result.
