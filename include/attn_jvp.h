@@ -62,7 +62,10 @@ typedef enum {
                                centring cancels where one key carries a row.
                                Tested within 2e-2 of tO's and O's largest
                                element up to scaled-logit standard deviations
-                               of 65-130 with tangent logits of tens */
+                               of 65-130 with tangent logits of tens; with
+                               tangent logits in the hundreds on peaky rows the
+                               bf16 rounding of P*tS (about 2^-9 |scale*tS| |V|)
+                               reached 2.1e-2 */
   ATTN_JVP_BF16_F32OUT = 2  /* bfloat16 inputs as ATTN_JVP_BF16, o and to written as
                                float32 (attn_jvp_fwd, attn_jvp_fwd_part); for
                                attn_jvp_merge: float32 partials, bfloat16 result.
