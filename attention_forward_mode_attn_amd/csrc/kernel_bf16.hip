@@ -23,8 +23,9 @@
 //    two ds_read_b64_tr_b16 transposing reads, whose 4-key runs match the
 //    accumulator layout of P, so V never needs an explicit transpose;
 //  * online softmax in the log2 domain with a lazily moved exponent base, per
-//    row running sums l = sum p and a = sum p*tS, and the epilogue
-//      O = acc_o / l,  tO = (acc_t - (a / l) acc_o) / l,  lse = (m + log2 l) ln 2;
+//    row running sums l = sum p (fp32), lb = sum bf16(p) and a = sum bf16(p*tS)
+//    (the weights and products the MFMAs consume), and the epilogue
+//      O = acc_o / lb,  tO = (acc_t - (a / lb) acc_o) / lb,  lse = (m + log2 l) ln 2;
 //  * software pipeline: iteration j computes the softmax of tile j under the
 //    logit MFMAs of tile j + 1 (phase A), then the product MFMAs of tile j
 //    while the logits of tile j + 1 leave their accumulators, already scaled
