@@ -145,12 +145,14 @@ __device__ inline int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r
 
 // Running per-query state.  m: max (log2 domain) used for exponentiation;
 // l, a: this lane's partial sums of p and p*tS over its half of the keys;
-// lb: of bf16(p), the weights the products consume (bf16 kernel only).
+// lb: of bf16(p), the weights the products consume; c: the value the tangent
+// logits are centred on (bf16 kernel only: a holds the sum of p*(tS - c)).
 struct RowState {
   float m;
   float l;
   float a;
   float lb;
+  float c;
 };
 
 // Mask keys >= valid (tile-relative) of a tile made of NB 32-key blocks.

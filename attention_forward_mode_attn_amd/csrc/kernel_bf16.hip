@@ -179,7 +179,7 @@ void attn_jvp_bf16_kernel(Params p) {
     acc_o[b] = f32x16{};
     acc_t[b] = f32x16{};
   }
-  RowState st = {-INFINITY, 0.0f, 0.0f, 0.0f};
+  RowState st = {-INFINITY, 0.0f, 0.0f, 0.0f, 0.0f};
   const float scale = p.scale;
   const float c2 = scale * kLog2e;
 
@@ -298,7 +298,7 @@ void attn_jvp_bf16_kernel(Params p) {
         yv[x] = __builtin_fmaf(tk.raw[x], c2, -st.m);
         pin(yv[x]);
       } else {
-        tsv[x - 32] = tk.raw[x] * scale;
+        tsv[x - 32] = __builtin_fmaf(tk.raw[x], scale, -st.c);
         pin(tsv[x - 32]);
       }
     } else if constexpr (x < 32) {
@@ -437,6 +437,34 @@ void attn_jvp_bf16_kernel(Params p) {
   constexpr int kUnitsB = (kFrozen ? 8 : 12) * C::kBlocksD;  // MFMAs of products(), 0 .. kUnitsB - 1
   constexpr int kSumAUnit = 3 - kPreSlots;  // first phase-B unit after the tile's last softmax step
 
+  // Tangent-logit centring (d = 128).  q = p (tS - c) is what gets rounded to
+  // bf16, so its rounding scales with |tS - c| rather than |tS|: when a tile
+  // moves a row's exponent base, c moves to that tile's weighted mean of tS (at
+  // the new base), and what was accumulated around the old c is re-expressed
+  // around the new one (acc_t -= dc acc_o, a -= dc lb: exact in the algebra).
+  // The tile's waiting logits (yv, tsv) are taken relative to the current base
+  // and c; rows with moved == false keep their c.  Outside the hot loop.  The
+  // one-tile-at-a-time loop of d = 64 keeps c = 0: there the step would sit in
+  // the tile loop, which it costs 59 registers and 4% of the time.
+  auto recentre = [&](bool moved) {
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int x = 0; x < 32; ++x) {
+      const float pw = fast_exp2(yv[x]);
+      num = __builtin_fmaf(pw, tsv[x], num);
+      den += pw;
+    }
+    num = xhalf_sum(num);
+    den = xhalf_sum(den);
+    const float dc = moved ? num / den : 0.0f;
+    st.c += dc;
+    st.a -= dc * st.lb;
+#pragma unroll
+    for (int x = 0; x < 32; ++x) tsv[x] -= dc;
+#pragma unroll
+    for (int b = 0; b < C::kBlocksD; ++b) acc_t[b] -= dc * acc_o[b];
+  };
+
   const int nt = (Lk + kBc - 1) / kBc;
   const bool ragged = (Lk % kBc) != 0;
   float my;  // row max of y over the tile waiting in (yv, tsv)
@@ -506,6 +534,7 @@ void attn_jvp_bf16_kernel(Params p) {
     st.m = tile_max_log2<2>(sn, c2);
     Take tk;
     all_steps(IC<0>{}, IC<64>{}, IC<2>{}, [&](auto is, auto ix) { take_step(is, ix, tk, sn, tsn); });
+    recentre(true);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): V|tV of tile 0 and K|tK of tile 1 landed
   __syncthreads();  // ... for every wave, and every wave is done with K of tile 0 before it is refilled
@@ -590,6 +619,7 @@ void attn_jvp_bf16_kernel(Params p) {
       acc_o[b] *= alpha;
       acc_t[b] *= alpha;
     }
+    recentre(delta > 0.0f);
   };
   auto needs_rescale = [&]() { return __builtin_amdgcn_ballot_w64(my > kRescaleSlack) != 0; };
 
@@ -710,7 +740,7 @@ void attn_jvp_bf16_kernel(Params p) {
     buf_store4(rl, (uint32_t)qrow * 4, (st.m + __builtin_amdgcn_logf(l)) * kLn2);
     if (p.tlse) {
       const auto rtl = make_rsrc((const char*)p.tlse + (size_t)bh * Lq * 4, (uint32_t)Lq * 4);
-      buf_store4(rtl, (uint32_t)qrow * 4, mu);
+      buf_store4(rtl, (uint32_t)qrow * 4, mu + st.c);
     }
   }
 }

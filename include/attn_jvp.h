@@ -60,12 +60,13 @@ typedef enum {
                                normalised by the sum of those bf16 weights (lse
                                by the float32 sum), so the tangent-logit
                                centring cancels where one key carries a row.
-                               Tested within 2e-2 of tO's and O's largest
-                               element up to scaled-logit standard deviations
-                               of 65-130 with tangent logits of tens; with
-                               tangent logits in the hundreds on peaky rows the
-                               bf16 rounding of P*tS (about 2^-9 |scale*tS| |V|)
-                               reached 2.1e-2 */
+                               At d = 128 the tangent logits are centred on a
+                               per-row value before P*tS is rounded, so its
+                               rounding scales with |scale*tS - c|, not
+                               |scale*tS|.  Tested within 2e-2 of tO's and O's
+                               largest element up to scaled-logit standard
+                               deviations of 65-130 and tangent logits in the
+                               hundreds */
   ATTN_JVP_BF16_F32OUT = 2  /* bfloat16 inputs as ATTN_JVP_BF16, o and to written as
                                float32 (attn_jvp_fwd, attn_jvp_fwd_part); for
                                attn_jvp_merge: float32 partials, bfloat16 result.

@@ -13,8 +13,9 @@ deviation 65-130, |lse| in the hundreds).  Representative cases:
   centring cancels for a dominant key; this case is checked at 2e-2;
 * bf16 rows with tangent logits in the hundreds (tangent std 5 on keys whose
   norms grow 30-fold): the bf16 rounding of P*tS, about 2^-9 |scale*tS| |V|,
-  exceeds the tolerance against the much smaller tO: an expected failure with
-  its measured error;
+  exceeded the tolerance against the much smaller tO (2.1e-2).  The kernel now
+  centres the tangent logits on a per-row value before that rounding (d = 128);
+  this case is checked at 2e-2;
 * float32 key shards: each shard's lse is a float32, so the merge weights
   carry a relative error of about 2^-24 |lse|; with |lse| near 1000 the merged
   O and tO are off by 1-2e-5 (the unsplit pass stays far inside 1e-5): an
@@ -85,12 +86,11 @@ def test_float32_shards_at_large_lse(A):
 def test_bf16_tangent_logits_in_the_hundreds(A):
     """Peaky rows (logit std ~9, key norms rising 30-fold along the keys) with
     tangent logits in the hundreds: P*tS meets V as bf16, so each product
-    carries about 2^-9 |scale*tS| |V| of rounding, while tO (the spread of tS
-    around its mean, times V) is far smaller; the worst head here is off by
-    2.1e-2 of the tensor's largest tO, unsplit and in key shards alike.  An fp32
-    emulation of the kernel's rounding puts the same head at 6.0e-2 and, with tS
-    centred on a per-row running value, at 4.0e-3 (but 40% worse on the stress
-    workload's rows); not built.  An expected failure with its measured error."""
+    carries about 2^-9 |scale*tS - c| |V| of rounding, while tO (the spread of
+    tS around its mean, times V) is far smaller.  Without centring (c = 0) the
+    worst head was off by 2.1e-2 of the tensor's largest tO; with tS centred on
+    the weighted mean of the tile that set each row's exponent base it is
+    within the tolerance, unsplit and in key shards alike."""
     std = {"q": 3.0, "k": 3.0, "v": 1.0, "tq": 5.0, "tk": 0.0, "tv": 0.0}
     w = custom_workload(1, 3, 25, 2999, 128, "bf16", seed_id=101735, std=std, key_ramp=0.01)
     print("case bf16 tangent logits in the hundreds B1 H3 Lq25 Lk2999 d128 frozen ramp0.01", flush=True)
@@ -104,9 +104,7 @@ def test_bf16_tangent_logits_in_the_hundreds(A):
     print(f"  unsplit O {whole['O']:.3e} tO {whole['tO']:.3e}; 2 shards O {split['O']:.3e} tO {split['tO']:.3e}",
           flush=True)
     for r in (whole, split):
-        assert r["O"] <= TOL["bf16"] and r["tO"] <= 0.1 and r["lse"] <= 1e-4
-    if max(whole["tO"], split["tO"]) > TOL["bf16"]:
-        pytest.xfail(f"bf16 P*tS rounding at |scale*tS| in the hundreds: tO {whole['tO']:.2e} > 2e-2")
+        assert r["O"] <= TOL["bf16"] and r["tO"] <= TOL["bf16"] and r["lse"] <= 1e-4
 
 
 def test_fp32_rows_carried_by_one_key(A):
